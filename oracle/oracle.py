@@ -1,0 +1,210 @@
+"""ctypes wrapper of the fp64 CPU oracle (pi0_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark.  Nothing in the product package imports it.
+
+All arrays are converted to contiguous float64 before the call; the oracle
+computes in double precision throughout.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pi0_oracle.c")
+_LIB = os.path.join(_HERE, "libpi0_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C11, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-D_GNU_SOURCE", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("width", "depth", "mlp_dim", "num_heads", "num_kv_heads",
+                                             "head_dim", "horizon", "action_dim", "state_dim")] + \
+               [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "min_period", "max_period")]
+
+
+_lib = None
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(_Cfg)
+        lib.pi0o_weight_count.argtypes = [P]
+        lib.pi0o_weight_count.restype = ctypes.c_size_t
+        lib.pi0o_set_threads.argtypes = [ctypes.c_int]
+        lib.pi0o_set_threads.restype = ctypes.c_int
+        lib.pi0o_sinusoid.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_double, _D]
+        lib.pi0o_rmsnorm.argtypes = [_D, _D, ctypes.c_int, ctypes.c_double, _D]
+        lib.pi0o_rope.argtypes = [_D, ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        lib.pi0o_gelu_tanh.argtypes = [ctypes.c_double]
+        lib.pi0o_gelu_tanh.restype = ctypes.c_double
+        lib.pi0o_silu.argtypes = [ctypes.c_double]
+        lib.pi0o_silu.restype = ctypes.c_double
+        lib.pi0o_attend_one.argtypes = [_D, ctypes.c_int, ctypes.c_double, _D, _D, ctypes.c_int, _D, _D,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_size_t, _D]
+        lib.pi0o_expert_layer.argtypes = [P, _D, _D, ctypes.c_int, _D, _D, ctypes.c_int, _D]
+        lib.pi0o_embed_suffix.argtypes = [P, _D, _D, _D, ctypes.c_double, _D]
+        lib.pi0o_expert_forward.argtypes = [P, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.pi0o_velocity.argtypes = [P, _D, _D, _D, ctypes.c_double, _D, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double, _D]
+        lib.pi0o_denoise.argtypes = [P, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_double, _D]
+        lib.pi0o_step_time.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.pi0o_step_time.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_D)
+
+
+def set_threads(n: int = 0) -> int:
+    """Set the OpenMP thread count (0 keeps the default); returns the count in use."""
+    return _load().pi0o_set_threads(int(n))
+
+
+def sinusoid(t: float, dim: int, min_period: float = 4e-3, max_period: float = 4.0) -> np.ndarray:
+    out = np.empty(dim, dtype=np.float64)
+    _load().pi0o_sinusoid(float(t), int(dim), float(min_period), float(max_period), _p(out))
+    return out
+
+
+def rmsnorm(h, w, eps: float = 1e-6) -> np.ndarray:
+    h, w = _f64(h), _f64(w)
+    out = np.empty_like(h)
+    _load().pi0o_rmsnorm(_p(h), _p(w), h.size, float(eps), _p(out))
+    return out
+
+
+def rope(u, pos: float, base: float = 10000.0) -> np.ndarray:
+    u = _f64(u).copy()
+    _load().pi0o_rope(_p(u), u.size, float(pos), float(base))
+    return u
+
+
+def gelu_tanh(x: float) -> float:
+    return _load().pi0o_gelu_tanh(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().pi0o_silu(float(x))
+
+
+def step_time(k: int, num_steps: int) -> float:
+    return _load().pi0o_step_time(int(k), int(num_steps))
+
+
+def attend_one(q, kp, vp, valid: int, ks, vs, r: int, scale: float) -> np.ndarray:
+    """One query row r of the suffix against prefix keys [0, valid) and the
+    suffix keys visible to r.  kp/vp: [L][dh], ks/vs: [S][dh]."""
+    q, kp, vp, ks, vs = _f64(q), _f64(kp), _f64(vp), _f64(ks), _f64(vs)
+    dh = q.size
+    out = np.empty(dh, dtype=np.float64)
+    _load().pi0o_attend_one(_p(q), dh, float(scale), _p(kp), _p(vp), int(valid), _p(ks), _p(vs),
+                            ks.shape[0], int(r), dh, _p(out))
+    return out
+
+
+class Oracle:
+    """fp64 oracle for one expert shape.  Weights are the flat blob (any float dtype)."""
+
+    def __init__(self, shape, weights):
+        s = shape
+        self.shape = s
+        self.cfg = _Cfg(s.width, s.depth, s.mlp_dim, s.num_heads, s.num_kv_heads, s.head_dim,
+                        s.horizon, s.action_dim, s.state_dim, s.rms_eps, s.rope_theta,
+                        s.min_period, s.max_period)
+        lib = _load()
+        n = lib.pi0o_weight_count(ctypes.byref(self.cfg))
+        w = _f64(weights)
+        if w.size != n:
+            raise ValueError(f"weight blob has {w.size} values, the shape needs {n}")
+        self.w = w
+
+    def _kv(self, kv_sample, L):
+        s = self.shape
+        kv = _f64(kv_sample)
+        if kv.size != s.depth * 2 * L * s.num_kv_heads * s.head_dim:
+            raise ValueError("prefix kv has the wrong size")
+        return kv
+
+    def layer(self, l: int, h, kp, vp, valid: int, pos) -> np.ndarray:
+        s = self.shape
+        h = _f64(h).copy()
+        kp, vp, pos = _f64(kp), _f64(vp), _f64(pos)
+        layer_size = (self.w.size - self._head_size()) // s.depth
+        wl = self.w[l * layer_size:(l + 1) * layer_size]
+        wl = np.ascontiguousarray(wl)
+        _load().pi0o_expert_layer(ctypes.byref(self.cfg), _p(wl), _p(h), h.shape[0], _p(kp), _p(vp),
+                                  int(valid), _p(pos))
+        return h
+
+    def _head_size(self):
+        s = self.shape
+        W, A, Sd = s.width, s.action_dim, s.state_dim
+        return W + W * Sd + W + W * A + W + W * 2 * W + W + W * W + W + A * W + A
+
+    def embed_suffix(self, state, x, t: float) -> np.ndarray:
+        s = self.shape
+        h = np.empty((s.suffix_len, s.width), dtype=np.float64)
+        _load().pi0o_embed_suffix(ctypes.byref(self.cfg), _p(self.w), _p(_f64(state)), _p(_f64(x)), float(t),
+                                  _p(h))
+        return h
+
+    def expert_forward(self, h, kv_sample, L: int, valid: int, pos_shift: float = 0.0) -> np.ndarray:
+        h = _f64(h).copy()
+        kv = self._kv(kv_sample, L)
+        _load().pi0o_expert_forward(ctypes.byref(self.cfg), _p(self.w), _p(h), _p(kv), int(L), int(valid),
+                                    float(pos_shift))
+        return h
+
+    def velocity(self, state, x, t: float, kv_sample, L: int, valid: int, pos_shift: float = 0.0) -> np.ndarray:
+        s = self.shape
+        v = np.empty((s.horizon, s.action_dim), dtype=np.float64)
+        kv = self._kv(kv_sample, L)
+        _load().pi0o_velocity(ctypes.byref(self.cfg), _p(self.w), _p(_f64(state)), _p(_f64(x)), float(t),
+                              _p(kv), int(L), int(valid), float(pos_shift), _p(v))
+        return v
+
+    def denoise(self, state, noise, kv_sample, L: int, valid: int, num_steps: int,
+                pos_shift: float = 0.0) -> np.ndarray:
+        """One sample: state [state_dim], noise [H][A], kv_sample [depth][2][L][n_kv][dh]."""
+        s = self.shape
+        out = np.empty((s.horizon, s.action_dim), dtype=np.float64)
+        kv = self._kv(kv_sample, L)
+        _load().pi0o_denoise(ctypes.byref(self.cfg), _p(self.w), _p(_f64(state)), _p(_f64(noise)), _p(kv),
+                             int(L), int(valid), int(num_steps), float(pos_shift), _p(out))
+        return out
+
+    def denoise_batch(self, inputs: dict, num_steps: int, samples=None) -> np.ndarray:
+        """Run samples (default: all) of a batch laid out as the boundary takes it."""
+        kv = inputs["prefix_kv"]
+        B, L = kv.shape[2], kv.shape[3]
+        idx = range(B) if samples is None else samples
+        outs = []
+        for b in idx:
+            outs.append(self.denoise(inputs["state"][b], inputs["noise"][b], kv[:, :, b], L,
+                                     int(inputs["valid_len"][b]), num_steps))
+        return np.stack(outs)

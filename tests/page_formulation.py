@@ -1,0 +1,154 @@
+"""A second, independent fp64 formulation of the pi0 expert denoise loop, used
+only to cross-check the C oracle on small shapes.
+
+It differs from the oracle in every place a slip could hide:
+- whole-tensor torch ops instead of per-row loops;
+- the Hugging Face Gemma modules that page 1
+  ("vllm_omni/diffusion/models/pi0/modeling_pi0.py") itself calls for the
+  q/k/v/o projections, the gate/up/down MLP with the tanh GELU and
+  apply_rotary_pos_emb, all in float64;
+- masking as an additive bias of the page's mask constant (-2.3819763e38)
+  built from the cumulative-sum visibility rule of make_att_2d_masks, rather
+  than skipping keys;
+- grouped-query attention by explicitly repeating the kv head to every query
+  head instead of indexing the shared head.
+
+Hugging Face's GemmaRMSNorm and rotary module evaluate internally in float32,
+so for a float64 comparison this formulation writes the Gemma norm
+(h / sqrt(mean(h^2) + eps) * (1 + w)) as one whole-tensor float64 expression
+and computes the rotary angles in float64 from HF's inverse-frequency
+definition (base^(-2j/d)); tests pin both against the HF modules to float32
+accuracy.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+from transformers import GemmaConfig
+from transformers.models.gemma.modeling_gemma import GemmaForCausalLM, apply_rotary_pos_emb
+
+from vla_flow_matching_amd import synth
+
+MASK_VALUE = -2.3819763e38
+
+
+def build_expert(shape: synth.ExpertShape, blob: np.ndarray) -> GemmaForCausalLM:
+    cfg = GemmaConfig(head_dim=shape.head_dim, hidden_size=shape.width, intermediate_size=shape.mlp_dim,
+                      num_attention_heads=shape.num_heads, num_hidden_layers=shape.depth,
+                      num_key_value_heads=shape.num_kv_heads, vocab_size=16, rms_norm_eps=shape.rms_eps,
+                      hidden_activation="gelu_pytorch_tanh", hidden_act="gelu_pytorch_tanh",
+                      rope_parameters={"rope_theta": shape.rope_theta, "rope_type": "default"})
+    m = GemmaForCausalLM(cfg).double().eval()
+    t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name), dtype=np.float64))
+    with torch.no_grad():
+        for l, layer in enumerate(m.model.layers):
+            layer.input_layernorm.weight.copy_(t(f"layers.{l}.input_norm"))
+            layer.self_attn.q_proj.weight.copy_(t(f"layers.{l}.q_proj"))
+            layer.self_attn.k_proj.weight.copy_(t(f"layers.{l}.k_proj"))
+            layer.self_attn.v_proj.weight.copy_(t(f"layers.{l}.v_proj"))
+            layer.self_attn.o_proj.weight.copy_(t(f"layers.{l}.o_proj"))
+            layer.post_attention_layernorm.weight.copy_(t(f"layers.{l}.post_norm"))
+            layer.mlp.gate_proj.weight.copy_(t(f"layers.{l}.gate_proj"))
+            layer.mlp.up_proj.weight.copy_(t(f"layers.{l}.up_proj"))
+            layer.mlp.down_proj.weight.copy_(t(f"layers.{l}.down_proj"))
+        m.model.norm.weight.copy_(t("final_norm"))
+    return m
+
+
+def rope_tables_f64(positions: torch.Tensor, head_dim: int, base: float):
+    """cos/sin [B, S, head_dim] for integer positions, angles in float64."""
+    inv_freq = 1.0 / (base ** (torch.arange(0, head_dim, 2, dtype=torch.float64) / head_dim))
+    ang = positions.to(torch.float64)[..., None] * inv_freq
+    ang = torch.cat([ang, ang], dim=-1)
+    return ang.cos(), ang.sin()
+
+
+def gemma_norm(h: torch.Tensor, w: torch.Tensor, eps: float) -> torch.Tensor:
+    return h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + eps) * (1.0 + w)
+
+
+def time_features(t: torch.Tensor, dim: int, min_p: float, max_p: float) -> torch.Tensor:
+    """[B, dim] sine/cosine features; log-spaced periods between min_p and max_p."""
+    frac = torch.linspace(0.0, 1.0, dim // 2, dtype=torch.float64)
+    omega = (2 * math.pi) / (min_p * (max_p / min_p) ** frac)
+    arg = t.to(torch.float64)[:, None] * omega[None, :]
+    return torch.cat([arg.sin(), arg.cos()], dim=1)
+
+
+class PageFormulation:
+    def __init__(self, shape: synth.ExpertShape, blob: np.ndarray):
+        self.s = shape
+        self.expert = build_expert(shape, blob)
+        t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name), dtype=np.float64))
+        self.lin = {}
+        for nm in ("state_proj", "action_in_proj", "action_time_mlp_in", "action_time_mlp_out", "action_out_proj"):
+            self.lin[nm] = (t(nm + ".weight"), t(nm + ".bias"))
+
+    def _linear(self, name, x):
+        w, b = self.lin[name]
+        return F.linear(x, w, b)
+
+    def suffix_embedding(self, state, x, t):
+        s = self.s
+        state_tok = self._linear("state_proj", state)[:, None, :]
+        tfeat = time_features(t, s.width, s.min_period, s.max_period)
+        act = self._linear("action_in_proj", x)
+        fused = torch.cat([act, tfeat[:, None, :].expand(-1, act.shape[1], -1)], dim=-1)
+        fused = self._linear("action_time_mlp_out", F.silu(self._linear("action_time_mlp_in", fused)))
+        return torch.cat([state_tok, fused], dim=1)
+
+    def visibility(self, valid: torch.Tensor, L: int) -> torch.Tensor:
+        """bool [B, S, L + S]: prefix key j visible iff j < valid; suffix key c visible
+        to query r iff cumsum(ar)[c] <= cumsum(ar)[r] with ar = [1, 1, 0, ..., 0]."""
+        S = self.s.suffix_len
+        B = valid.shape[0]
+        pre = (torch.arange(L)[None, :] < valid[:, None])[:, None, :].expand(B, S, L)
+        ar = torch.zeros(S, dtype=torch.int64)
+        ar[:2] = 1
+        cum = torch.cumsum(ar, 0)
+        suf = (cum[None, :] <= cum[:, None])[None].expand(B, S, S)
+        return torch.cat([pre, suf], dim=2)
+
+    def velocity(self, state, x, t, kv, valid):
+        """state [B, Sd], x [B, H, A], t [B], kv [depth, 2, B, L, n_kv, dh], valid [B] -> v [B, H, A]."""
+        s = self.s
+        B, L = kv.shape[2], kv.shape[3]
+        h = self.suffix_embedding(state, x, t)
+        bias = torch.where(self.visibility(valid, L), 0.0, MASK_VALUE).to(torch.float64)[:, None]
+        pos = valid[:, None].to(torch.int64) + torch.arange(s.suffix_len)[None, :]
+        cos, sin = rope_tables_f64(pos, s.head_dim, s.rope_theta)
+        rep = s.num_heads // s.num_kv_heads
+        for l, layer in enumerate(self.expert.model.layers):
+            att = layer.self_attn
+            y = gemma_norm(h, layer.input_layernorm.weight, s.rms_eps)
+            q = att.q_proj(y).view(B, -1, s.num_heads, s.head_dim).transpose(1, 2)
+            k = att.k_proj(y).view(B, -1, s.num_kv_heads, s.head_dim).transpose(1, 2)
+            v = att.v_proj(y).view(B, -1, s.num_kv_heads, s.head_dim).transpose(1, 2)
+            q, k = apply_rotary_pos_emb(q, k, cos, sin, unsqueeze_dim=1)
+            kp = kv[l, 0].permute(0, 2, 1, 3)   # [B, n_kv, L, dh]
+            vp = kv[l, 1].permute(0, 2, 1, 3)
+            k = torch.cat([kp, k], dim=2).repeat_interleave(rep, dim=1)
+            v = torch.cat([vp, v], dim=2).repeat_interleave(rep, dim=1)
+            scores = q @ k.transpose(-1, -2) / math.sqrt(s.head_dim) + bias
+            o = torch.softmax(scores, dim=-1) @ v
+            o = o.transpose(1, 2).reshape(B, s.suffix_len, s.num_heads * s.head_dim)
+            h = h + att.o_proj(o)
+            h = h + layer.mlp(gemma_norm(h, layer.post_attention_layernorm.weight, s.rms_eps))
+        h = gemma_norm(h, self.expert.model.norm.weight, s.rms_eps)
+        return self._linear("action_out_proj", h[:, 1:])
+
+    def denoise(self, inputs: dict, num_steps: int) -> np.ndarray:
+        f = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
+        kv, valid = f(inputs["prefix_kv"]), torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
+        kv = torch.nan_to_num(kv, nan=0.0)  # additive masking multiplies padding by 0; keep it finite
+        state, x = f(inputs["state"]), f(inputs["noise"])
+        B = state.shape[0]
+        with torch.no_grad():
+            for k in range(num_steps):
+                tk = float(np.float32(1.0 - k / num_steps))
+                v = self.velocity(state, x, torch.full((B,), tk, dtype=torch.float64), kv, valid)
+                x = x + (-1.0 / num_steps) * v
+        return x.numpy()

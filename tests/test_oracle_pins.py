@@ -1,0 +1,417 @@
+"""Pins of the fp64 CPU oracle to what the pages and the mathematics fix.
+
+Each test checks one oracle function against something other than itself:
+a closed form, an invariant, a library routine (torch / scipy / the Hugging
+Face Gemma modules that page 1 "vllm_omni/diffusion/models/pi0/
+modeling_pi0.py" calls), brute force, or an independent second formulation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle
+from vla_flow_matching_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+TINY = synth.TINY
+
+
+# ----------------------------------------------------------------------------
+# Sinusoidal time embedding (page 1, create_sinusoidal_pos_embedding)
+# ----------------------------------------------------------------------------
+def test_sinusoid_t0_closed_form():
+    out = oracle.sinusoid(0.0, 1024)
+    assert np.array_equal(out[:512], np.zeros(512))
+    assert np.array_equal(out[512:], np.ones(512))
+
+
+def test_sinusoid_t1_endpoints():
+    # omega_0 = 2*pi / 4e-3 = 500*pi, omega_511 = 2*pi / 4.0 = pi / 2
+    out = oracle.sinusoid(1.0, 1024)
+    assert abs(out[0]) < 1e-12 and abs(out[512] - 1.0) < 1e-15
+    assert abs(out[511] - 1.0) < 1e-15 and abs(out[1023]) < 1e-15
+
+
+def test_sinusoid_log_spaced_frequencies():
+    # for tiny t, sin(omega t) ~ omega t: the frequencies form a geometric sequence
+    # from 2*pi/min_period down to 2*pi/max_period (ratio 1000^(1/511)).
+    t = 1e-9
+    om = oracle.sinusoid(t, 1024)[:512] / t
+    assert om[0] == pytest.approx(2 * math.pi / 4e-3, rel=1e-9)
+    assert om[-1] == pytest.approx(2 * math.pi / 4.0, rel=1e-9)
+    ratios = om[:-1] / om[1:]
+    assert np.allclose(ratios, 1000.0 ** (1.0 / 511), rtol=1e-8)
+
+
+def test_sinusoid_pythagoras():
+    out = oracle.sinusoid(0.37, 256)
+    assert np.allclose(out[:128] ** 2 + out[128:] ** 2, 1.0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm with the (1 + w) scale (Hugging Face GemmaRMSNorm)
+# ----------------------------------------------------------------------------
+def test_rmsnorm_w0_rms_closed_form():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal(1024)
+    y = oracle.rmsnorm(h, np.zeros(1024), 1e-6)
+    ms = np.mean(h * h)
+    assert math.sqrt(np.mean(y * y)) == pytest.approx(1.0 / math.sqrt(1.0 + 1e-6 / ms), rel=1e-13)
+
+
+def test_rmsnorm_one_plus_w_and_scale_invariance():
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal(512)
+    y0 = oracle.rmsnorm(h, np.zeros(512), 0.0)
+    assert np.allclose(oracle.rmsnorm(h, np.ones(512), 0.0), 2.0 * y0, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.rmsnorm(37.5 * h, np.zeros(512), 0.0), y0, rtol=1e-14)
+
+
+def test_rmsnorm_matches_hf_gemma_rmsnorm():
+    from transformers.models.gemma.modeling_gemma import GemmaRMSNorm
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((5, 256))
+    w = rng.standard_normal(256) * 0.3
+    m = GemmaRMSNorm(256, eps=1e-6).double()
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(w))
+        ref = m(torch.from_numpy(h)).numpy()
+    ours = np.stack([oracle.rmsnorm(h[i], w, 1e-6) for i in range(5)])
+    # HF evaluates the norm in float32 internally (x.float()), hence the float32-level bar
+    assert np.allclose(ours, ref, rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Rotary embedding (rotate-half; page 1 calls HF apply_rotary_pos_emb)
+# ----------------------------------------------------------------------------
+def test_rope_identity_at_zero_and_norm_preserved():
+    rng = np.random.default_rng(4)
+    u = rng.standard_normal(256)
+    assert np.array_equal(oracle.rope(u, 0.0), u)
+    for p in (1.0, 17.0, 866.0):
+        assert np.linalg.norm(oracle.rope(u, p)) == pytest.approx(np.linalg.norm(u), rel=1e-14)
+
+
+def test_rope_unit_vectors_closed_form():
+    # R_p e_j = cos(theta_j) e_j + sin(theta_j) e_{j+d/2}, theta_j = p * base^(-2j/d);
+    # at j = 0 the angle is p itself, at j = d/4 it is p / sqrt(base) = p / 100.
+    d, p = 256, 3.0
+    for j, theta in ((0, p), (64, p / 100.0)):
+        e = np.zeros(d)
+        e[j] = 1.0
+        r = oracle.rope(e, p)
+        exp = np.zeros(d)
+        exp[j], exp[j + d // 2] = math.cos(theta), math.sin(theta)
+        assert np.allclose(r, exp, atol=1e-15)
+
+
+def test_rope_relative_position_invariance():
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal(256), rng.standard_normal(256)
+    base = np.dot(oracle.rope(q, 40.0), oracle.rope(k, 7.0))
+    for c in (1.0, 13.0, 500.0):
+        assert np.dot(oracle.rope(q, 40.0 + c), oracle.rope(k, 7.0 + c)) == pytest.approx(base, rel=1e-11, abs=1e-11)
+
+
+def test_rope_matches_hf_apply_rotary_pos_emb():
+    from transformers.models.gemma.modeling_gemma import apply_rotary_pos_emb
+    from tests.page_formulation import rope_tables_f64
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, 4, 32))
+    pos = torch.tensor([[0, 5, 64, 71]])
+    cos, sin = rope_tables_f64(pos, 32, 10000.0)
+    ref, _ = apply_rotary_pos_emb(torch.from_numpy(q), torch.from_numpy(q), cos, sin)
+    ours = np.stack([oracle.rope(q[0, 0, i], float(pos[0, i])) for i in range(4)])
+    assert np.allclose(ours, ref[0, 0].numpy(), atol=1e-14)
+
+
+def test_rope_table_matches_hf_rotary_module():
+    # the float64 table used by the second formulation agrees with HF's own
+    # (float32-angle) rotary module to float32 accuracy
+    from transformers import GemmaConfig
+    from transformers.models.gemma.modeling_gemma import GemmaRotaryEmbedding
+    from tests.page_formulation import rope_tables_f64
+    cfg = GemmaConfig(head_dim=256, hidden_size=1024, num_attention_heads=8, num_key_value_heads=1)
+    rot = GemmaRotaryEmbedding(cfg)
+    pos = torch.arange(0, 900, 7)[None]
+    cos, sin = rot(torch.zeros(1, 1, 256, dtype=torch.float64), pos)
+    c64, s64 = rope_tables_f64(pos, 256, 10000.0)
+    assert torch.allclose(cos, c64, atol=2e-4) and torch.allclose(sin, s64, atol=2e-4)
+
+
+# ----------------------------------------------------------------------------
+# Activations
+# ----------------------------------------------------------------------------
+def test_gelu_tanh_matches_torch_and_erf_bound():
+    xs = np.linspace(-8, 8, 161)
+    ours = np.array([oracle.gelu_tanh(x) for x in xs])
+    ref = F.gelu(torch.from_numpy(xs), approximate="tanh").numpy()
+    assert np.allclose(ours, ref, rtol=1e-14, atol=1e-15)
+    exact = 0.5 * xs * (1.0 + scipy.special.erf(xs / math.sqrt(2.0)))
+    assert np.max(np.abs(ours - exact)) < 1e-3   # the tanh form approximates erf-GELU within 1e-3
+    assert oracle.gelu_tanh(0.0) == 0.0
+
+
+def test_silu_matches_torch():
+    xs = np.linspace(-30, 30, 121)
+    ours = np.array([oracle.silu(x) for x in xs])
+    assert np.allclose(ours, F.silu(torch.from_numpy(xs)).numpy(), rtol=1e-14, atol=1e-300)
+
+
+# ----------------------------------------------------------------------------
+# Attention: visibility, masking, softmax
+# ----------------------------------------------------------------------------
+def _attn_case(seed=7, L=12, S=5, dh=16):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(dh), rng.standard_normal((L, dh)), rng.standard_normal((L, dh)),
+            rng.standard_normal((S, dh)), rng.standard_normal((S, dh)))
+
+
+def test_attention_uniform_closed_form():
+    # q = 0 => every visible score is 0 => output is the plain mean of the visible values.
+    # The state row (r = 0) sees valid prefix keys and itself; action rows see valid
+    # prefix keys, the state token and every action token.
+    _, kp, vp, ks, vs = _attn_case()
+    q = np.zeros(16)
+    for valid in (0, 1, 7, 12):
+        o0 = oracle.attend_one(q, kp, vp, valid, ks, vs, 0, 0.25)
+        assert np.allclose(o0, np.concatenate([vp[:valid], vs[:1]]).mean(0), atol=1e-15)
+        for r in (1, 4):
+            o = oracle.attend_one(q, kp, vp, valid, ks, vs, r, 0.25)
+            assert np.allclose(o, np.concatenate([vp[:valid], vs]).mean(0), atol=1e-15)
+
+
+def test_attention_state_row_valid0_is_own_value():
+    q, kp, vp, ks, vs = _attn_case()
+    assert np.array_equal(oracle.attend_one(q, kp, vp, 0, ks, vs, 0, 0.25), vs[0])
+
+
+def test_attention_masked_keys_contribute_zero():
+    q, kp, vp, ks, vs = _attn_case()
+    valid = 7
+    ref = oracle.attend_one(q, kp, vp, valid, ks, vs, 2, 0.25)
+    kp2, vp2 = kp.copy(), vp.copy()
+    kp2[valid:], vp2[valid:] = np.nan, 1e30
+    assert np.array_equal(oracle.attend_one(q, kp2, vp2, valid, ks, vs, 2, 0.25), ref)
+
+
+def test_attention_matches_torch_sdpa_brute_force():
+    q, kp, vp, ks, vs = _attn_case(seed=8, L=9, S=6, dh=8)
+    valid = 6
+    for r in range(6):
+        keys = np.concatenate([kp, ks])
+        vals = np.concatenate([vp, vs])
+        vis = np.zeros(len(keys), dtype=bool)
+        vis[:valid] = True
+        vis[len(kp)] = True                     # the state token
+        if r >= 1:
+            vis[len(kp):] = True                # every suffix token
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None], torch.from_numpy(keys)[None, None],
+            torch.from_numpy(vals)[None, None], attn_mask=torch.from_numpy(vis)[None, None, None], scale=0.3)
+        ours = oracle.attend_one(q, kp, vp, valid, ks, vs, r, 0.3)
+        assert np.allclose(ours, ref.numpy().ravel(), rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Layer, embedding, loop
+# ----------------------------------------------------------------------------
+def _tiny_blob(seed=0, **kw):
+    return synth.make_weights(TINY, seed=seed, **kw).astype(np.float64)
+
+
+def _zero_expert(blob, shape):
+    b = blob.copy()
+    for name, _ in synth.blob_layout(shape):
+        if name.startswith("layers."):
+            synth.view(b, shape, name)[...] = 0.0
+    return b
+
+
+def test_zero_weight_layer_is_identity():
+    blob = _zero_expert(_tiny_blob(), TINY)
+    o = oracle.Oracle(TINY, blob)
+    rng = np.random.default_rng(9)
+    h = rng.standard_normal((TINY.suffix_len, TINY.width))
+    kp, vp = rng.standard_normal((2, 64, TINY.head_dim))
+    out = o.layer(0, h, kp, vp, 64, np.arange(TINY.suffix_len) + 64.0)
+    assert np.array_equal(out, h)
+
+
+def test_layer_uniform_attention_closed_form():
+    # W_k = 0, prefix K = 0 and zero MLP: the layer adds W_o applied to the mean of
+    # the visible values (identical for every head).
+    s = TINY
+    blob = _tiny_blob(seed=3)
+    for nm in ("k_proj", "gate_proj", "up_proj", "down_proj"):
+        synth.view(blob, s, f"layers.0.{nm}")[...] = 0.0
+    o = oracle.Oracle(s, blob)
+    rng = np.random.default_rng(10)
+    h = rng.standard_normal((s.suffix_len, s.width))
+    L, valid = 20, 13
+    kp = np.zeros((L, s.head_dim))
+    vp = rng.standard_normal((L, s.head_dim))
+    out = o.layer(0, h, kp, vp, valid, np.arange(s.suffix_len) + float(valid))
+    y = np.stack([oracle.rmsnorm(h[r], synth.view(blob, s, "layers.0.input_norm"), s.rms_eps)
+                  for r in range(s.suffix_len)])
+    vs = y @ synth.view(blob, s, "layers.0.v_proj").T
+    wo = synth.view(blob, s, "layers.0.o_proj")
+    for r in range(s.suffix_len):
+        vis = np.concatenate([vp[:valid], vs[:1] if r == 0 else vs])
+        att = np.tile(vis.mean(0), s.num_heads)
+        assert np.allclose(out[r] - h[r], wo @ att, atol=1e-12)
+
+
+def test_embed_time_mlp_zero_input_weights_closed_form():
+    s = TINY
+    blob = _tiny_blob(seed=4)
+    synth.view(blob, s, "action_time_mlp_in.weight")[...] = 0.0
+    o = oracle.Oracle(s, blob)
+    rng = np.random.default_rng(11)
+    state, x = rng.standard_normal(s.state_dim), rng.standard_normal((s.horizon, s.action_dim))
+    h = o.embed_suffix(state, x, 0.6)
+    bmi = synth.view(blob, s, "action_time_mlp_in.bias")
+    row = synth.view(blob, s, "action_time_mlp_out.weight") @ (bmi / (1 + np.exp(-bmi))) + \
+        synth.view(blob, s, "action_time_mlp_out.bias")
+    assert np.allclose(h[1:], row[None], atol=1e-13)
+    assert np.allclose(h[0], synth.view(blob, s, "state_proj.weight") @ state + synth.view(blob, s, "state_proj.bias"),
+                       atol=1e-13)
+
+
+def test_step_times():
+    for n in (1, 2, 5, 10):
+        for k in range(n):
+            assert oracle.step_time(k, n) == float(np.float32(1.0 - k / n))
+    assert [oracle.step_time(k, 5) for k in range(5)] == [float(np.float32(v)) for v in (1.0, 0.8, 0.6, 0.4, 0.2)]
+
+
+def _tiny_inputs(seed=0, valid=None, L=64, batch=1):
+    w = synth.WORKLOADS["tiny_fp32_b1"].replace(seed=seed, batch=batch, prefix_len=L)
+    inp = synth.make_inputs(w)
+    if valid is not None:
+        inp["valid_len"][:] = valid
+    return inp
+
+
+def test_constant_velocity_euler_exact():
+    # W_out = 0 => v = b_out at every step => x_N = noise + sum_k dt * b_out, accumulated
+    # step by step exactly as the sampler does.
+    s = TINY
+    blob = _tiny_blob(seed=5)
+    synth.view(blob, s, "action_out_proj.weight")[...] = 0.0
+    b = synth.view(blob, s, "action_out_proj.bias").copy()
+    inp = _tiny_inputs()
+    o = oracle.Oracle(s, blob)
+    for n in (1, 3, 10):
+        out = o.denoise_batch(inp, n)[0]
+        x = inp["noise"][0].astype(np.float64)
+        for _ in range(n):
+            x = x + (-1.0 / n) * b[None, :]
+        assert np.array_equal(out, x)
+
+
+def test_single_step_is_noise_minus_velocity_at_t1():
+    s = TINY
+    blob = _tiny_blob(seed=6)
+    inp = _tiny_inputs(seed=1)
+    o = oracle.Oracle(s, blob)
+    out = o.denoise_batch(inp, 1)[0]
+    v = o.velocity(inp["state"][0], inp["noise"][0], 1.0, inp["prefix_kv"][:, :, 0], 64, 64)
+    assert np.array_equal(out, inp["noise"][0] - v)
+
+
+def test_zero_expert_reduces_to_head_closed_form():
+    # zero expert layers + W_mi = 0: every action row is the same constant c, so
+    # v = W_out rmsnorm(c) + b_out for every row and step; the loop returns noise - v.
+    s = TINY
+    blob = _zero_expert(_tiny_blob(seed=7), s)
+    synth.view(blob, s, "action_time_mlp_in.weight")[...] = 0.0
+    bmi = synth.view(blob, s, "action_time_mlp_in.bias")
+    c = synth.view(blob, s, "action_time_mlp_out.weight") @ (bmi / (1 + np.exp(-bmi))) + \
+        synth.view(blob, s, "action_time_mlp_out.bias")
+    hf = c / np.sqrt(np.mean(c * c) + s.rms_eps)
+    v = synth.view(blob, s, "action_out_proj.weight") @ hf + synth.view(blob, s, "action_out_proj.bias")
+    inp = _tiny_inputs(seed=2)
+    out = oracle.Oracle(s, blob).denoise_batch(inp, 4)[0]
+    assert np.allclose(out, inp["noise"][0] - v[None, :], atol=1e-12)
+
+
+def test_padding_is_never_read():
+    s = TINY
+    blob = _tiny_blob(seed=8)
+    inp = _tiny_inputs(seed=3, valid=41)
+    o = oracle.Oracle(s, blob)
+    ref = o.denoise_batch(inp, 2)
+    inp2 = dict(inp)
+    kv = inp["prefix_kv"].copy()
+    kv[:, :, :, 41:] = np.nan
+    inp2["prefix_kv"] = kv
+    assert np.array_equal(o.denoise_batch(inp2, 2), ref)
+
+
+def test_rope_invariance_end_to_end():
+    # raw prefix keys rotated at positions j + c, suffix positions shifted by c:
+    # attention only sees relative positions, so the chunk is unchanged.
+    s = TINY
+    blob = _tiny_blob(seed=9)
+    inp = _tiny_inputs(seed=4)
+    raw = inp["prefix_kv"].astype(np.float64)
+    o = oracle.Oracle(s, blob)
+
+    def rotated(c):
+        kv = raw.copy()
+        for l in range(s.depth):
+            for j in range(64):
+                kv[l, 0, 0, j, 0] = oracle.rope(raw[l, 0, 0, j, 0], j + c, s.rope_theta)
+        return kv[:, :, 0]
+
+    ref = o.denoise(inp["state"][0], inp["noise"][0], rotated(0.0), 64, 64, 2)
+    for c in (5.0, 300.0):
+        out = o.denoise(inp["state"][0], inp["noise"][0], rotated(c), 64, 64, 2, pos_shift=c)
+        assert np.allclose(out, ref, atol=1e-11)
+
+
+def test_state_row_independent_of_actions_and_time():
+    s = TINY
+    blob = _tiny_blob(seed=10)
+    inp = _tiny_inputs(seed=5)
+    o = oracle.Oracle(s, blob)
+    kv = inp["prefix_kv"][:, :, 0]
+    rng = np.random.default_rng(12)
+    h1 = o.expert_forward(o.embed_suffix(inp["state"][0], inp["noise"][0], 1.0), kv, 64, 50)
+    h2 = o.expert_forward(o.embed_suffix(inp["state"][0], rng.standard_normal((s.horizon, s.action_dim)), 0.3),
+                          kv, 64, 50)
+    assert np.array_equal(h1[0], h2[0])
+    assert not np.allclose(h1[1:], h2[1:])
+
+
+@pytest.mark.parametrize("valid", [64, 23, 0])
+def test_oracle_matches_page_formulation_tiny(valid):
+    from tests.page_formulation import PageFormulation
+    s = TINY
+    blob = synth.make_weights(s, seed=11, norm_std=0.2)
+    inp = _tiny_inputs(seed=6, valid=valid, batch=2)
+    ref = PageFormulation(s, blob).denoise(inp, 3)
+    ours = oracle.Oracle(s, blob).denoise_batch(inp, 3)
+    assert np.max(np.abs(ours - ref)) < 1e-11
+
+
+def test_oracle_matches_page_formulation_gqa_two_kv_heads():
+    # grouped-query attention with 2 kv heads: explicit repeat vs shared-head indexing
+    from tests.page_formulation import PageFormulation
+    s = synth.ExpertShape(width=128, depth=2, mlp_dim=256, num_heads=4, num_kv_heads=2, head_dim=32,
+                          horizon=5, action_dim=8, state_dim=6)
+    blob = synth.make_weights(s, seed=12, norm_std=0.1)
+    w = synth.Workload("gqa", s, "fp32", 2, 16, 2, seed=7)
+    inp = synth.make_inputs(w)
+    inp["valid_len"][:] = [16, 9]
+    ref = PageFormulation(s, blob).denoise(inp, 2)
+    ours = oracle.Oracle(s, blob).denoise_batch(inp, 2)
+    assert np.max(np.abs(ours - ref)) < 1e-11
