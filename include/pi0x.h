@@ -1,0 +1,151 @@
+/*
+ * pi0x.h -- C ABI of the pi0 action-expert flow-matching denoise loop on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page 1, "vllm_omni/diffusion/models/pi0/modeling_pi0.py",
+ * sections sample_actions, denoise_step, embed_suffix and
+ * _compute_layer_suffix_only): given the per-layer key/value cache of an
+ * observation prefix, a proprioceptive state and Gaussian noise, integrate
+ * the flow-matching ODE from t = 1 to t = 0 with num_steps explicit Euler
+ * steps (dt = -1/num_steps, t_k = 1 + k*dt, x <- x + dt * v_t) and return the
+ * action chunk x of shape (batch, horizon, action_dim).  Each velocity v_t
+ * embeds the suffix [state token ; horizon action tokens fused with a
+ * sinusoidal embedding of t through a swish MLP], runs the Gemma-shaped
+ * action expert whose attention reads the cached prefix keys/values plus the
+ * block-causal suffix, applies the final RMSNorm to the action rows and
+ * projects them with action_out_proj.
+ *
+ * Every entry point is plain C: host pointers for configuration and weights,
+ * device pointers for activations, a HIP stream for ordering.  All device
+ * work runs in the library's own HIP kernels.
+ *
+ * Errors: every function returns a pi0x_status.  Argument errors are found on
+ * the host before anything is enqueued; pi0x_last_error() then returns a
+ * thread-local message.  Device-side failures surface when the caller
+ * synchronises the stream.
+ */
+#ifndef PI0X_H_
+#define PI0X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PI0X_OK = 0,
+  PI0X_ERR_INVALID_ARG = -1, /* null pointer, non-positive count, bad config value */
+  PI0X_ERR_SHAPE = -2,       /* a shape the kernels do not support (see pi0x_config) */
+  PI0X_ERR_DTYPE = -3,       /* unknown dtype */
+  PI0X_ERR_OOM = -4,         /* device allocation failed */
+  PI0X_ERR_HIP = -5,         /* a HIP runtime call failed */
+  PI0X_ERR_CAPACITY = -6     /* batch, prefix length or steps above what the handle was created for */
+} pi0x_status;
+
+typedef enum {
+  PI0X_FP32 = 0, /* float32 weights, activations and prefix K/V */
+  PI0X_BF16 = 1  /* bfloat16 weights, activations and prefix K/V, float32 accumulation,
+                    float32 residual stream and action state */
+} pi0x_dtype;
+
+/*
+ * Expert shape and capacity.  The pi0 action expert is get_gemma_config
+ * ("gemma_300m") on page 1: width 1024, depth 18, mlp 4096, 8 query heads,
+ * 1 kv head, head_dim 256; horizon 50, action_dim 32, state_dim 32 are the
+ * page's defaults.  Supported by the kernels: num_kv_heads == 1, head_dim a
+ * multiple of 32 and at most 256, width and mlp_dim multiples of 64,
+ * num_heads * head_dim a multiple of 64, action_dim and state_dim at most 64.
+ */
+typedef struct {
+  int32_t width, depth, mlp_dim, num_heads, num_kv_heads, head_dim;
+  int32_t action_horizon, action_dim, state_dim;
+  int32_t max_batch;      /* largest batch a call may pass */
+  int32_t max_prefix_len; /* largest padded prefix length a call may pass */
+  int32_t max_steps;      /* largest num_steps a call may pass */
+  float rms_eps;          /* Gemma RMSNorm epsilon (1e-6) */
+  float rope_theta;       /* rotary base (10000, the Gemma default) */
+  float time_min_period;  /* sinusoidal time embedding periods (4e-3, 4.0 on page 1) */
+  float time_max_period;
+  int32_t dtype;          /* pi0x_dtype */
+  int32_t use_graphs;     /* 1: replay the N-step loop as one captured hipGraph; 0: launch eagerly */
+} pi0x_config;
+
+typedef struct pi0x_expert pi0x_expert;
+
+/* Fills *cfg with the pi0 action-expert shape above, max_batch 64,
+ * max_prefix_len 1024, max_steps 64, bf16, graphs on. */
+void pi0x_config_default(pi0x_config* cfg);
+
+/* Number of float32 values in the weight blob for cfg (0 if cfg is invalid).
+ * Blob layout, every matrix [out_features][in_features] like nn.Linear:
+ *   per layer l = 0..depth-1:
+ *     input_norm[W], q_proj[H*D][W], k_proj[D][W], v_proj[D][W], o_proj[W][H*D],
+ *     post_norm[W], gate_proj[M][W], up_proj[M][W], down_proj[W][M]
+ *   final_norm[W],
+ *   state_proj.weight[W][Sd], state_proj.bias[W],
+ *   action_in_proj.weight[W][A], action_in_proj.bias[W],
+ *   action_time_mlp_in.weight[W][2W], action_time_mlp_in.bias[W]   (input = [action ; time]),
+ *   action_time_mlp_out.weight[W][W], action_time_mlp_out.bias[W],
+ *   action_out_proj.weight[A][W], action_out_proj.bias[A]
+ * with W = width, H = num_heads, D = head_dim, M = mlp_dim, A = action_dim,
+ * Sd = state_dim.  Norm weights w enter as (1 + w) (Gemma RMSNorm). */
+size_t pi0x_weight_count(const pi0x_config* cfg);
+
+/* Creates a handle on the current HIP device.  weights_host: host float32
+ * blob of pi0x_weight_count(cfg) values (weights_bytes must equal 4x that);
+ * it is copied, repacked and converted to cfg->dtype (round to nearest even),
+ * so the caller may free it on return.  The handle owns every device buffer
+ * it needs for calls up to the capacities in cfg.  On error *out is NULL. */
+pi0x_status pi0x_expert_create(const pi0x_config* cfg, const void* weights_host, size_t weights_bytes,
+                               pi0x_expert** out);
+
+/*
+ * Full denoise loop (page 1, sample_actions after the prefix pass).
+ *   prefix_kv        device, cfg dtype, [depth][2][batch][prefix_len][head_dim]:
+ *                    per layer the keys (index 0, already rotary-embedded at
+ *                    their prefix positions) and values (index 1) of the
+ *                    single kv head.  Read only.
+ *   prefix_valid_len device int32 [batch]: keys [0, v) of sample b are real,
+ *                    [v, prefix_len) are padding and are never read.  Values
+ *                    outside [0, prefix_len] are clamped into it.  The suffix
+ *                    tokens take rotary positions v, v+1, ..., v+horizon.
+ *   state            device float32 [batch][state_dim].
+ *   noise            device float32 [batch][horizon][action_dim]: x at t = 1.
+ *   num_steps        >= 1 and <= cfg->max_steps.
+ *   actions_out      device float32 [batch][horizon][action_dim]: x at t = 0.
+ *                    May alias noise; must not overlap the other inputs.
+ *   stream           HIP stream the work is ordered on (0 = null stream).
+ * Asynchronous: returns after enqueueing.  One handle serves one stream at a
+ * time: calls on the same handle from different threads or streams race on
+ * its workspaces. */
+pi0x_status pi0x_denoise(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                         const int32_t* prefix_valid_len, const float* state, const float* noise,
+                         int32_t num_steps, float* actions_out, hipStream_t stream);
+
+/*
+ * One velocity evaluation (page 1, denoise_step): v = v_theta(x_t, t) for
+ * every sample, with the same prefix/state arguments as pi0x_denoise.
+ *   x_t    device float32 [batch][horizon][action_dim]
+ *   t      time value (the sampler uses 1 + k*dt rounded to float32)
+ *   v_out  device float32 [batch][horizon][action_dim]; must not overlap inputs.
+ */
+pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                              const int32_t* prefix_valid_len, const float* state, const float* x_t, float t,
+                              float* v_out, hipStream_t stream);
+
+/* Releases the handle and everything it owns (synchronises the device first).
+ * NULL is ignored. */
+void pi0x_expert_destroy(pi0x_expert* h);
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* pi0x_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI0X_H_ */

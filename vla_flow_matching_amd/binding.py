@@ -1,0 +1,195 @@
+"""ctypes binding of libpi0x.so (include/pi0x.h).
+
+Argument marshalling only: every step of the denoise loop runs in the
+library's HIP kernels.  The module-level functions carry the C names and
+take raw integers for device pointers and streams; ``Expert`` wraps them for
+torch device tensors.  Loading fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpi0x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pi0x.h")
+
+PI0X_OK = 0
+PI0X_ERR_INVALID_ARG = -1
+PI0X_ERR_SHAPE = -2
+PI0X_ERR_DTYPE = -3
+PI0X_ERR_OOM = -4
+PI0X_ERR_HIP = -5
+PI0X_ERR_CAPACITY = -6
+PI0X_FP32 = 0
+PI0X_BF16 = 1
+
+
+class pi0x_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "width", "depth", "mlp_dim", "num_heads", "num_kv_heads", "head_dim",
+        "action_horizon", "action_dim", "state_dim", "max_batch", "max_prefix_len", "max_steps")] + \
+        [(n, ctypes.c_float) for n in ("rms_eps", "rope_theta", "time_min_period", "time_max_period")] + \
+        [("dtype", ctypes.c_int32), ("use_graphs", ctypes.c_int32)]
+
+
+class Pi0xError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"pi0x status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/pi0x.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(pi0x_[a-z_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(the HIP library is required, there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(pi0x_config)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.pi0x_config_default.argtypes = [P]
+        L.pi0x_config_default.restype = None
+        L.pi0x_weight_count.argtypes = [P]
+        L.pi0x_weight_count.restype = sz
+        L.pi0x_expert_create.argtypes = [P, vp, sz, ctypes.POINTER(vp)]
+        L.pi0x_expert_create.restype = i32
+        L.pi0x_denoise.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.pi0x_denoise.restype = i32
+        L.pi0x_denoise_step.argtypes = [vp, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+        L.pi0x_denoise_step.restype = i32
+        L.pi0x_expert_destroy.argtypes = [vp]
+        L.pi0x_expert_destroy.restype = None
+        L.pi0x_last_error.argtypes = []
+        L.pi0x_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# --- the C entry points, same names -----------------------------------------
+def pi0x_config_default() -> pi0x_config:
+    c = pi0x_config()
+    lib().pi0x_config_default(ctypes.byref(c))
+    return c
+
+
+def pi0x_weight_count(cfg: pi0x_config) -> int:
+    return lib().pi0x_weight_count(ctypes.byref(cfg))
+
+
+def pi0x_last_error() -> str:
+    return lib().pi0x_last_error().decode()
+
+
+def pi0x_expert_create(cfg: pi0x_config, weights_ptr: int, weights_bytes: int) -> tuple[int, int]:
+    h = ctypes.c_void_p()
+    st = lib().pi0x_expert_create(ctypes.byref(cfg), weights_ptr, weights_bytes, ctypes.byref(h))
+    return st, (h.value or 0)
+
+
+def pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream) -> int:
+    return lib().pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream)
+
+
+def pi0x_denoise_step(h, batch, prefix_len, prefix_kv, valid, state, x_t, t, v_out, stream) -> int:
+    return lib().pi0x_denoise_step(h, batch, prefix_len, prefix_kv, valid, state, x_t, float(t), v_out, stream)
+
+
+def pi0x_expert_destroy(h) -> None:
+    lib().pi0x_expert_destroy(h)
+
+
+def check(status: int) -> None:
+    if status != PI0X_OK:
+        raise Pi0xError(status, pi0x_last_error())
+
+
+def make_config(shape, dtype: str = "bf16", max_batch: int = 64, max_prefix_len: int = 1024,
+                max_steps: int = 64, use_graphs: bool = True) -> pi0x_config:
+    c = pi0x_config()
+    c.width, c.depth, c.mlp_dim = shape.width, shape.depth, shape.mlp_dim
+    c.num_heads, c.num_kv_heads, c.head_dim = shape.num_heads, shape.num_kv_heads, shape.head_dim
+    c.action_horizon, c.action_dim, c.state_dim = shape.horizon, shape.action_dim, shape.state_dim
+    c.max_batch, c.max_prefix_len, c.max_steps = max_batch, max_prefix_len, max_steps
+    c.rms_eps, c.rope_theta = shape.rms_eps, shape.rope_theta
+    c.time_min_period, c.time_max_period = shape.min_period, shape.max_period
+    c.dtype = PI0X_BF16 if dtype == "bf16" else PI0X_FP32
+    c.use_graphs = 1 if use_graphs else 0
+    return c
+
+
+class Expert:
+    """Owns a pi0x handle; calls take torch device tensors."""
+
+    def __init__(self, cfg: pi0x_config, weights: np.ndarray):
+        import torch  # noqa: F401  (device memory and streams come from torch)
+        w = np.ascontiguousarray(weights, dtype=np.float32)
+        self.cfg = cfg
+        st, self.h = pi0x_expert_create(cfg, w.ctypes.data, w.nbytes)
+        check(st)
+
+    def _stream(self, stream):
+        import torch
+        return (stream or torch.cuda.current_stream()).cuda_stream
+
+    @staticmethod
+    def _ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    def denoise(self, prefix_kv, valid_len, state, noise, num_steps: int, out=None, stream=None):
+        import torch
+        B = state.shape[0]
+        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
+        if out is None:
+            out = torch.empty_like(noise)
+        check(pi0x_denoise(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
+                           self._ptr(noise), int(num_steps), self._ptr(out), self._stream(stream)))
+        return out
+
+    def denoise_step(self, prefix_kv, valid_len, state, x_t, t: float, out=None, stream=None):
+        import torch
+        B = state.shape[0]
+        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
+        if out is None:
+            out = torch.empty_like(x_t)
+        check(pi0x_denoise_step(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
+                                self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
+        return out
+
+    def close(self):
+        if getattr(self, "h", 0):
+            pi0x_expert_destroy(self.h)
+            self.h = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def device_inputs(inputs: dict, dtype: str, device: str = "cuda"):
+    """Copy host inputs (synth.make_inputs) to device tensors in the boundary's layout:
+    prefix_kv [depth][2][B][L][head_dim] in the model dtype, the rest as given."""
+    import torch
+    kv = inputs["prefix_kv"]
+    kv = kv.reshape(kv.shape[0], kv.shape[1], kv.shape[2], kv.shape[3], -1)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {
+        "prefix_kv": torch.from_numpy(np.ascontiguousarray(kv)).to(device=device, dtype=tdt),
+        "valid_len": torch.from_numpy(np.ascontiguousarray(inputs["valid_len"], dtype=np.int32)).to(device),
+        "state": torch.from_numpy(np.ascontiguousarray(inputs["state"], dtype=np.float32)).to(device),
+        "noise": torch.from_numpy(np.ascontiguousarray(inputs["noise"], dtype=np.float32)).to(device),
+    }

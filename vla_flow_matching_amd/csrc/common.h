@@ -1,0 +1,124 @@
+// Shared device-side types and helpers for the pi0x kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pi0x {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// Per-call arguments that change between calls without re-recording the
+// captured graph.  A one-thread kernel writes this struct on the caller's
+// stream right before the graph replays; every kernel reads its pointers here.
+struct CallDesc {
+  const void* kv;        // prefix K/V, [depth][2][B][L][head_dim], model dtype
+  const int32_t* valid;  // [B] valid prefix lengths
+  const float* state;    // [B][state_dim]
+  const float* x_in;     // denoise: the noise (x at t = 1); single step: x_t.  [B][H][A]
+  float* out;            // denoise: the actions; single step: the velocity.  [B][H][A]
+  float t;               // single step: the time value
+};
+
+// float -> bfloat16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  uint16_t r;
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) {
+    r = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r = (uint16_t)(u >> 16);
+  }
+  return __builtin_bit_cast(bf16, r);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { return f2bf(f); }
+
+__device__ __forceinline__ float to_f32(float f) { return f; }
+__device__ __forceinline__ float to_f32(bf16 b) {
+  return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A "k32 fragment" is what one lane contributes to a 16x16
+// output tile for a 32-wide slice of the reduction dimension: lane l covers
+// row/column (l % 16) and the 8 reduction indices 8*(l/16) .. 8*(l/16)+7.
+// bf16 issues one v_mfma_f32_16x16x32_bf16; fp32 issues eight
+// v_mfma_f32_16x16x4_f32, the i-th taking reduction index 8*(l/16)+i (the
+// two operands only have to agree on which index each lane supplies).
+// Output tile layout (both): lane l holds rows 4*(l/16)+e, e = 0..3, of
+// column l % 16.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma32(const Frag<bf16>& a, const Frag<bf16>& b, f32x4& c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(const Frag<float>& a, const Frag<float>& b, f32x4& c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], c, 0, 0, 0);
+}
+
+// 8 consecutive elements
+__device__ __forceinline__ void load8(Frag<bf16>& f, const bf16* p) { f.v = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// 4 + 4 consecutive elements from two places
+__device__ __forceinline__ void load4x2(Frag<bf16>& f, const bf16* p0, const bf16* p1) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+__device__ __forceinline__ void load4x2(Frag<float>& f, const float* p0, const float* p1) {
+  float4 a = *reinterpret_cast<const float4*>(p0);
+  float4 b = *reinterpret_cast<const float4*>(p1);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void set_frag(Frag<bf16>& f, int i, float x) { f.v[i] = f2bf(x); }
+__device__ __forceinline__ void set_frag(Frag<float>& f, int i, float x) { f.v[i] = x; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * x * (1.0f + tanhf(k * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Deterministic split reduction support: a block that finishes its share of a
+// tile bumps the tile's arrival counter; the block that arrives last gets
+// true, sums every share in a fixed order and resets the counter to 0 for the
+// next launch.  Every block of the tile calls it exactly once.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int tid) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    unsigned prev = atomicAdd(counter, 1u);
+    s_last = (prev == expected - 1u);
+  }
+  __syncthreads();
+  if (!s_last) return false;
+  __threadfence();
+  return true;
+}
+
+}  // namespace pi0x
