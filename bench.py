@@ -1,0 +1,209 @@
+"""Benchmark of the pi0 action-expert denoise loop on one MI355X.
+
+One "step" is one pi0x_denoise call: the whole num_steps-Euler loop over one
+batch of synthetic inputs already resident in device memory, replayed from its
+captured hipGraph.  The default workload is the bf16 pi0 expert at batch 64
+(prefix 816, horizon 50 x 32, 10 Euler steps); the batch-1 latency workload
+is measured in the same run and reported under "b1".
+
+Output: one JSON line with the throughput (action chunks/s), the roofline
+figure of the dominant kernel (per-launch algorithmic bytes or flops over its
+average duration, from HIP events around that kernel's launches in an eager
+pass of the same loop), and the fp64 CPU oracle timed on a bounded sample on
+this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "action chunks/s, 10-step π0 expert denoise at B=1 & B=64; % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP32_PEAK_TFS = 157.3   # MI355X fp32 matrix
+BALANCE = 312.5              # flop per byte at which bf16 MFMA and HBM peaks meet
+
+
+def algorithmic_counts(shape, batch: int, valid: np.ndarray, num_steps: int, esz: int):
+    """Bytes and flops of one denoise call, counted as the method defines it:
+    every expert and head weight once per Euler step, the visible prefix K/V
+    once per step, the action state in and out; 51 suffix tokens per sample and
+    only visible keys in attention.  Intermediates are not counted."""
+    from vla_flow_matching_amd import synth
+    s = shape
+    params = synth.weight_count(s)
+    kv_bytes = int(np.sum(valid)) * s.depth * 2 * s.num_kv_heads * s.head_dim * esz
+    io = batch * s.horizon * s.action_dim * 4 * 2 + batch * s.state_dim * 4
+    bytes_step = params * esz + kv_bytes
+    W, M, qd, kd = s.width, s.mlp_dim, s.num_heads * s.head_dim, s.num_kv_heads * s.head_dim
+    dense_params = s.depth * (W * (qd + 2 * kd) + qd * W + 3 * M * W)
+    S = s.suffix_len
+    dense = 2.0 * dense_params * S * batch
+    per_pair = 4.0 * s.head_dim  # q.k and p*v multiply-adds per (query head, key)
+    attn = 0.0
+    for v in valid:
+        attn += s.depth * s.num_heads * per_pair * (s.horizon * (int(v) + S) + (int(v) + 1))
+    head = 2.0 * batch * (s.state_dim * W + s.horizon * (s.action_dim * W + 2 * W * W + W * W + W * s.action_dim))
+    return {"bytes": bytes_step * num_steps + io, "flops": (dense + attn + head) * num_steps,
+            "bytes_per_step": bytes_step, "flops_per_step": dense + attn + head}
+
+
+def kernel_unit_counts(shape, batch: int, esz: int, valid: np.ndarray):
+    """Algorithmic bytes and flops of one launch of each kernel class."""
+    s = shape
+    W, M, qd, dh = s.width, s.mlp_dim, s.num_heads * s.head_dim, s.head_dim
+    R = batch * s.suffix_len
+    nqkv = qd + 2 * dh
+    vis = float(np.sum(valid)) / max(batch, 1)
+    return {
+        "gate_up": {"bytes": (2 * M * W + R * W + R * M) * esz, "flops": 2.0 * R * 2 * M * W},
+        "down": {"bytes": (W * M + R * M) * esz + R * W * 4 * 2, "flops": 2.0 * R * W * M},
+        "qkv_rope": {"bytes": (nqkv * W + R * W + R * nqkv) * esz, "flops": 2.0 * R * nqkv * W},
+        "o_proj": {"bytes": (W * qd + R * qd) * esz + R * W * 4 * 2, "flops": 2.0 * R * W * qd},
+        "attention": {"bytes": (batch * vis * 2 * dh + R * (qd + 2 * dh) + R * qd) * esz,
+                      "flops": batch * s.num_heads * 4.0 * dh * (s.horizon * (vis + s.suffix_len) + vis + 1)},
+    }
+
+
+def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
+    import torch
+    from vla_flow_matching_amd import binding, synth
+
+    w = synth.WORKLOADS[name]
+    s = w.shape
+    esz = 2 if w.dtype == "bf16" else 4
+    blob = synth.make_weights(s, seed=w.seed, dtype=w.dtype)
+    inputs = synth.make_inputs(w)
+    cfg = binding.make_config(s, w.dtype, max_batch=w.batch, max_prefix_len=w.prefix_len, max_steps=w.num_steps)
+    ex = binding.Expert(cfg, blob)
+    del blob
+    d = binding.device_inputs(inputs, w.dtype)
+    out = torch.empty_like(d["noise"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ex.denoise(d["prefix_kv"], d["valid_len"], d["state"], d["noise"], w.num_steps, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    assert np.all(np.isfinite(out.cpu().numpy())), "non-finite actions"
+
+    # per-kernel durations: the same loop launched eagerly with HIP events
+    ex.set_timing(True)
+    for _ in range(timing_calls):
+        call()
+    timing = ex.read_timing()
+    ex.set_timing(False)
+    ex.close()
+
+    valid = inputs["valid_len"]
+    counts = algorithmic_counts(s, w.batch, valid, w.num_steps, esz)
+    units = kernel_unit_counts(s, w.batch, esz, valid)
+    kern = {}
+    for k, (tot, n) in timing.items():
+        if n:
+            kern[k] = {"avg_us": 1e3 * tot / n, "launches_per_call": n // timing_calls,
+                       "share": tot / max(sum(t for t, _ in timing.values()), 1e-12)}
+    dom = max((k for k in kern if k in units), key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_call"])
+    u = units[dom]
+    avg_s = kern[dom]["avg_us"] * 1e-6
+    intensity = u["flops"] / u["bytes"]
+    if intensity < BALANCE:
+        roof = {"bound": "hbm", "achieved": u["bytes"] / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        peak = MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS
+        roof = {"bound": "mfma", "achieved": u["flops"] / avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["per_launch"] = {"bytes": u["bytes"], "flops": u["flops"], "avg_us": kern[dom]["avg_us"]}
+    sec = ms * 1e-3
+    whole = {"achieved_GBps": counts["bytes"] / sec / 1e9, "hbm_frac": counts["bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+             "achieved_TFLOPs": counts["flops"] / sec / 1e12,
+             "mfma_frac": counts["flops"] / sec / 1e12 / (MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS),
+             "bytes_per_call": counts["bytes"], "flops_per_call": counts["flops"]}
+    return {"workload": w, "ms": ms, "value": w.batch / sec, "roofline": roof, "kernels": kern, "whole_loop": whole,
+            "inputs": inputs}
+
+
+def cpu_baseline(w, inputs, budget_s: float = 12.0):
+    """fp64 oracle on this host's cores: sequential velocity evaluations of
+    sample 0's chunk until the budget is spent (at most one whole chunk)."""
+    from oracle import oracle
+    from vla_flow_matching_amd import synth
+    cores = len(os.sched_getaffinity(0))
+    threads = oracle.set_threads(cores)
+    blob = synth.make_weights(w.shape, seed=w.seed, dtype=w.dtype)
+    o = oracle.Oracle(w.shape, blob)
+    del blob
+    kv = inputs["prefix_kv"][:, :, 0]
+    L, v = w.prefix_len, int(inputs["valid_len"][0])
+    x = inputs["noise"][0].astype(np.float64)
+    dt = -1.0 / w.num_steps
+    n, t0 = 0, time.perf_counter()
+    while n < w.num_steps and (n == 0 or time.perf_counter() - t0 < budget_s):
+        vel = o.velocity(inputs["state"][0], x, oracle.step_time(n, w.num_steps), kv, L, v)
+        x = x + dt * vel
+        n += 1
+    per_eval = (time.perf_counter() - t0) / n
+    return {"value": 1.0 / (per_eval * w.num_steps), "unit": "chunks/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of the {w.num_steps} Euler velocity evaluations of sample 0 (L={L}, valid {v}), "
+                      f"fp64, {per_eval:.2f} s each; chunks/s = 1 / ({w.num_steps} x time per evaluation)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="pi0_bf16_b64")
+    ap.add_argument("--b1-workload", default="pi0_bf16_b1", help="secondary latency workload ('' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the denoise loop shards by "
+              f"sample with no exchange, so N GPUs run N independent copies)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    main_res = run_workload(args.workload, args.steps, args.warmup)
+    w = main_res["workload"]
+    line = {
+        "metric": METRIC, "value": main_res["value"], "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prefix_len": w.prefix_len, "num_steps": w.num_steps,
+                   "horizon": w.shape.horizon, "action_dim": w.shape.action_dim, "expert": "gemma_300m shape"},
+        "roofline": main_res["roofline"],
+        "whole_loop": main_res["whole_loop"],
+        "kernels": main_res["kernels"],
+    }
+    if args.b1_workload:
+        r = run_workload(args.b1_workload, max(args.steps, 20), args.warmup)
+        line["b1"] = {"workload": r["workload"].name, "chunks_per_s": r["value"], "latency_ms": r["ms"],
+                      "roofline": r["roofline"], "whole_loop": r["whole_loop"], "kernels": r["kernels"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, main_res["inputs"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,9 +56,9 @@ typedef enum {
  * Expert shape and capacity.  The pi0 action expert is get_gemma_config
  * ("gemma_300m") on page 1: width 1024, depth 18, mlp 4096, 8 query heads,
  * 1 kv head, head_dim 256; horizon 50, action_dim 32, state_dim 32 are the
- * page's defaults.  Supported by the kernels: num_kv_heads == 1, head_dim a
- * multiple of 32 and at most 256, width and mlp_dim multiples of 64,
- * num_heads * head_dim a multiple of 64, action_dim and state_dim at most 64.
+ * page's defaults.  Supported by the kernels: num_kv_heads == 1, head_dim in
+ * {32, 64, 128, 256}, width a multiple of 256, mlp_dim and num_heads *
+ * head_dim multiples of 128, action_dim and state_dim at most 64.
  */
 typedef struct {
   int32_t width, depth, mlp_dim, num_heads, num_kv_heads, head_dim;
@@ -143,6 +143,30 @@ void pi0x_expert_destroy(pi0x_expert* h);
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pi0x_last_error(void);
+
+/*
+ * Kernel timing, for benchmarks.  While enabled, calls on the handle run
+ * eagerly (the same kernels with the same arguments as the recorded graph,
+ * launched one by one) and every launch of the classes below is bracketed by
+ * a pair of HIP events on the call's stream.  pi0x_read_timing synchronises
+ * with the last recorded event, writes per-class total milliseconds and launch
+ * counts (arrays of PI0X_KERNEL_CLASSES entries) and clears the record.
+ */
+typedef enum {
+  PI0X_KERNEL_SUFFIX_EMBED = 0, /* time features, state token, time MLP */
+  PI0X_KERNEL_RMSNORM = 1,      /* (unused: the norms are fused into the projections) */
+  PI0X_KERNEL_QKV_ROPE = 2,     /* q/k/v projection + RoPE */
+  PI0X_KERNEL_ATTENTION = 3,    /* prefix + suffix GQA attention (and the per-call transpose
+                                   of the prefix values) */
+  PI0X_KERNEL_O_PROJ = 4,       /* o_proj + residual */
+  PI0X_KERNEL_GATE_UP = 5,      /* gate/up projection + GeGLU */
+  PI0X_KERNEL_DOWN = 6,         /* down projection + residual */
+  PI0X_KERNEL_FINAL = 7,        /* final norm + action_out_proj + Euler update */
+  PI0X_KERNEL_CLASSES = 8
+} pi0x_kernel_class;
+
+pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable);
+pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

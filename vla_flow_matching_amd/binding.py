@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.pi0x_expert_destroy.restype = None
         L.pi0x_last_error.argtypes = []
         L.pi0x_last_error.restype = ctypes.c_char_p
+        L.pi0x_set_timing.argtypes = [vp, i32]
+        L.pi0x_set_timing.restype = i32
+        L.pi0x_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.pi0x_read_timing.restype = i32
         _lib = L
     return _lib
 
@@ -109,6 +113,21 @@ def pi0x_denoise_step(h, batch, prefix_len, prefix_kv, valid, state, x_t, t, v_o
 
 def pi0x_expert_destroy(h) -> None:
     lib().pi0x_expert_destroy(h)
+
+
+KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final"]
+
+
+def pi0x_set_timing(h, enable: bool) -> int:
+    return lib().pi0x_set_timing(h, 1 if enable else 0)
+
+
+def pi0x_read_timing(h) -> tuple[int, dict]:
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    st = lib().pi0x_read_timing(h, ms, cnt)
+    return st, {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
 
 
 def check(status: int) -> None:
@@ -167,6 +186,14 @@ class Expert:
         check(pi0x_denoise_step(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                                 self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
         return out
+
+    def set_timing(self, enable: bool):
+        check(pi0x_set_timing(self.h, enable))
+
+    def read_timing(self) -> dict:
+        st, t = pi0x_read_timing(self.h)
+        check(st)
+        return t
 
     def close(self):
         if getattr(self, "h", 0):

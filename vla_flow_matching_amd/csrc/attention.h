@@ -3,22 +3,23 @@
 // denoise_step): every suffix query sees the valid prefix keys j < valid_len;
 // inside the suffix the state token (s = 0) sees only itself and every action
 // token (s >= 1) sees the state token and all action tokens.  One kv head is
-// shared by all query heads, so the num_heads * S queries of a sample form one
-// [num_heads*S][head_dim] matrix against a single key/value sequence.
+// shared by all query heads, so the num_heads * S queries of a sample (query
+// index qi = s*num_heads + n) form one matrix against one key/value sequence.
 //
-// Block = 4 waves = 64 queries (query index qi = s*num_heads + n), grid
-// (query tiles, batch, key splits).  Keys are visited in blocks of 32: a block
-// of K (row-major) and V (transposed) is staged in LDS once and used by all 4
-// waves.  Each wave computes S^T = K Q^T with the matrix cores, so a lane holds
-// 8 scores of its own query (lane % 16); the online softmax runs in float32
-// entirely in registers, and O^T = V^T P^T reuses those 8 probabilities as the
-// MFMA operand directly (no transpose through LDS).  Masked keys are skipped
-// exactly: padded prefix keys are never loaded (zeros are staged) and their
-// probabilities are exactly 0.
+// Keys are visited in blocks of 32.  A wave computes S^T = K Q^T with the
+// matrix cores, so a lane holds 8 scores of its own query (lane % 16); the
+// online softmax runs in float32 in registers, and O^T = V^T P^T reuses those
+// 8 probabilities directly as the MFMA operand.  V is read transposed
+// ([head_dim][keys]): the prefix values are transposed once per call by
+// transpose_v_kernel, the suffix values are written transposed by the q/k/v
+// projection.  Masked keys get probability exactly 0; padded prefix keys are
+// never read from the caller's cache (zeros are used instead).
 //
-// With splits > 1 the key blocks of a sample are divided over gridDim.z; every
-// split writes (running max, running sum, unnormalised O) and the last split
-// to arrive merges them in split order.
+// attn_kernel: 4 waves x 16 queries share each staged K / V^T block in LDS
+// (large batches).  attn_small_kernel: 8 waves split the key blocks of the
+// same 16 queries, load operands straight from L2, and merge their partial
+// softmax states through LDS at the end (batch 1, where 64-query tiles would
+// leave most of the chip idle).
 #pragma once
 
 #include "common.h"
@@ -26,55 +27,104 @@
 namespace pi0x {
 
 struct AttnArgs {
-  const void* qkv;   // [B*S][ldqkv]: q heads at column 0, k at qk_k, v at qk_v
-  int ldqkv, col_k, col_v;
+  const void* qk;  // [B*S][ldqk]: q heads at column 0, the k head at col_k
+  int ldqk, col_k;
   const CallDesc* desc;
-  size_t kv_k_off, kv_v_off;  // element offsets of this layer's K and V blocks inside desc->kv
+  size_t kv_k_off;  // element offset of this layer's prefix K block inside desc->kv
+  const void* vtp;  // this layer's prefix V^T: [B][head_dim][Lp], zero beyond valid_len
+  int Lp;
+  const void* vts;  // suffix V^T: [B][head_dim][Sp], zero beyond S
+  int Sp;
   int B, L, S, nh;
   void* out;  // [B*S][ldo], head n of token s at column n*head_dim
   int ldo;
   float scale;
-  int splits;
-  float* partial;      // splits > 1: [B*tiles][splits][(2 + DH/4) * 256]
-  unsigned* counters;  // splits > 1: [B*tiles]
 };
 
-// exp for the softmax: the hardware exp2 path in bf16 mode, the accurate
-// libm expf in float32 mode.
+// exp for the softmax: the hardware exp2 path in bf16 mode, libm expf in float32 mode.
 template <typename T> __device__ __forceinline__ float fexp(float x) { return expf(x); }
 template <> __device__ __forceinline__ float fexp<bf16>(float x) { return __expf(x); }
 
+// Per-wave online-softmax state for 16 queries (lane % 16) and head_dim DH.
+template <typename T, int DH>
+struct SoftmaxState {
+  static constexpr int ND = DH / 16;
+  f32x4 o[ND];
+  float m = -INFINITY, l = 0.f;  // running max (same on the 4 lanes of a query), this lane's share of the sum
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // st[kt][e]: score of this lane's query vs key kt*16 + 4g + e of the block (already masked to -inf).
+  // Returns the probabilities as the PV operand (key order (e/4)*16 + 4g + e%4).
+  __device__ __forceinline__ Frag<T> update(const float (&s)[8]) {
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bmax = fmaxf(bmax, s[i]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float m_new = fmaxf(m, bmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fexp<T>(m - m_new);
+    Frag<T> pf;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = (s[i] == -INFINITY) ? 0.f : fexp<T>(s[i] - m_new);
+      l += e;
+      set_frag(pf, i, e);
+    }
+    m = m_new;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      o[d][0] *= alpha; o[d][1] *= alpha; o[d][2] *= alpha; o[d][3] *= alpha;
+    }
+    return pf;
+  }
+};
+
+// Scores of one 32-key block, masked: keys >= lim do not exist; in the suffix
+// (pre == false) the state query (qs == 0) only sees key 0.
+__device__ __forceinline__ void mask_scores(const f32x4 (&st)[2], float scale, int base, int lim, bool pre, int qs,
+                                            int g, float (&s)[8]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = base + kt * 16 + g * 4 + e;
+      bool vis = key < lim;
+      if (!pre) vis = vis && (qs >= 1 || key == 0);
+      s[kt * 4 + e] = vis ? st[kt][e] * scale : -INFINITY;
+    }
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int KB = 32;                  // keys per block
-  constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  constexpr int LDK = DH + VE;             // padded K row
-  constexpr int LDV = KB + VE;             // padded V^T row
-  constexpr int NC = DH / 32;              // 32-wide chunks of head_dim
-  constexpr int ND = DH / 16;              // 16-wide output tiles of head_dim
+  constexpr int KB = 32;
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int LDK = DH + VE;  // padded K row
+  constexpr int LDV = KB + VE;  // padded V^T row
+  constexpr int NC = DH / 32, ND = DH / 16;
   __shared__ __attribute__((aligned(16))) T Ks[KB * LDK];
   __shared__ __attribute__((aligned(16))) T Vt[DH * LDV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int tile = blockIdx.x, b = blockIdx.y;
   const int nq = a.nh * a.S;
   const int qi = tile * 64 + wave * 16 + (lane & 15);
   const bool qok = qi < nq;
   const int qs = qok ? qi / a.nh : 0, qn = qok ? qi - qs * a.nh : 0;
-  const int g = lane >> 4;
 
   int valid = a.desc->valid[b];
   valid = valid < 0 ? 0 : (valid > a.L ? a.L : valid);
-  const T* __restrict__ qkv = reinterpret_cast<const T*>(a.qkv);
-  const T* __restrict__ kvb = reinterpret_cast<const T*>(a.desc->kv);
-  const T* Kp = kvb + a.kv_k_off + (size_t)b * a.L * DH;
-  const T* Vp = kvb + a.kv_v_off + (size_t)b * a.L * DH;
-  const T* Sbase = qkv + (size_t)b * a.S * a.ldqkv;
+  const T* __restrict__ qk = reinterpret_cast<const T*>(a.qk);
+  const T* Kp = reinterpret_cast<const T*>(a.desc->kv) + a.kv_k_off + (size_t)b * a.L * DH;
+  const T* Vtp = reinterpret_cast<const T*>(a.vtp) + (size_t)b * DH * a.Lp;
+  const T* Vts = reinterpret_cast<const T*>(a.vts) + (size_t)b * DH * a.Sp;
+  const T* Sq = qk + (size_t)b * a.S * a.ldqk;
 
-  // this lane's query: 8 elements per 32-wide chunk, for the S^T = K Q^T operand
   Frag<T> qf[NC];
   {
-    const T* qrow = Sbase + (size_t)qs * a.ldqkv + qn * DH;
+    const T* qrow = Sq + (size_t)qs * a.ldqk + qn * DH;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (qok) load8(qf[c], qrow + c * 32 + g * 8);
@@ -83,51 +133,40 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int i = 0; i < 8; ++i) set_frag(qf[c], i, 0.f);
     }
   }
-
   const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
-  const int nblk = nb_pre + nb_suf;
-  const int blk_b = (int)((long)split * nblk / a.splits), blk_e = (int)((long)(split + 1) * nblk / a.splits);
+  SoftmaxState<T, DH> sm;
+  sm.init();
 
-  f32x4 o[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-
-  for (int blk = blk_b; blk < blk_e; ++blk) {
+  for (int blk = 0; blk < nb_pre + nb_suf; ++blk) {
     const bool pre = blk < nb_pre;
-    const int base = pre ? blk * KB : (blk - nb_pre) * KB;  // first key of the block
-    const int lim = pre ? valid : a.S;                        // keys >= lim do not exist
-    // ---- stage K (row-major) and V^T ----
-    constexpr int VPR = DH / VE;  // vectors per key row
+    const int base = pre ? blk * KB : (blk - nb_pre) * KB;
+    const int lim = pre ? valid : a.S;
+    constexpr int KVPR = DH / VE;  // 16-byte vectors per K row
 #pragma unroll
-    for (int it = 0; it < (KB * VPR + 255) / 256; ++it) {
+    for (int it = 0; it < (KB * KVPR + 255) / 256; ++it) {
       const int v = tid + it * 256;
-      if (v < KB * VPR) {
-        // K: chunk index fastest -> coalesced global reads, contiguous LDS rows
-        const int kk = v / VPR, dc = v - kk * VPR;
-        const int key = base + kk;
+      if (v < KB * KVPR) {
+        const int kk = v / KVPR, dc = v - kk * KVPR, key = base + kk;
         uint4 val = make_uint4(0, 0, 0, 0);
         if (key < lim) {
-          const T* src = pre ? Kp + (size_t)key * DH : Sbase + (size_t)key * a.ldqkv + a.col_k;
+          const T* src = pre ? Kp + (size_t)key * DH : Sq + (size_t)key * a.ldqk + a.col_k;
           val = *reinterpret_cast<const uint4*>(src + dc * VE);
         }
         *reinterpret_cast<uint4*>(&Ks[kk * LDK + dc * VE]) = val;
-        // V: key index fastest -> conflict-free transposed LDS writes
-        const int kv2 = v % KB, dc2 = v / KB;
-        const int key2 = base + kv2;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (key2 < lim) {
-          const T* src = pre ? Vp + (size_t)key2 * DH : Sbase + (size_t)key2 * a.ldqkv + a.col_v;
-          w = *reinterpret_cast<const uint4*>(src + dc2 * VE);
-        }
-        const T* wv = reinterpret_cast<const T*>(&w);
+      }
+    }
+    constexpr int VPR = KB / VE;  // 16-byte vectors per V^T row of the block
 #pragma unroll
-        for (int i = 0; i < VE; ++i) Vt[(dc2 * VE + i) * LDV + kv2] = wv[i];
+    for (int it = 0; it < (DH * VPR + 255) / 256; ++it) {
+      const int v = tid + it * 256;
+      if (v < DH * VPR) {
+        const int d = v / VPR, kc = (v - d * VPR) * VE;
+        const T* src = pre ? Vtp + (size_t)d * a.Lp + base + kc : Vts + (size_t)d * a.Sp + base + kc;
+        *reinterpret_cast<uint4*>(&Vt[d * LDV + kc]) = *reinterpret_cast<const uint4*>(src);
       }
     }
     __syncthreads();
 
-    // ---- scores: S^T tiles for keys 0..15 and 16..31 of the block ----
     f32x4 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -139,85 +178,163 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         mma32(kf, qf[c], st[kt]);
       }
     }
-    // lane holds score of its query vs key kt*16 + 4g + e
-    float p[8];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = base + kt * 16 + g * 4 + e;
-        bool vis = key < lim;
-        if (!pre) vis = vis && (qs >= 1 || key == 0);
-        const float s = vis ? st[kt][e] * a.scale : -INFINITY;
-        p[kt * 4 + e] = s;
-        bmax = fmaxf(bmax, s);
-      }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fexp<T>(m_run - m_new);
-    Frag<T> pf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e = (p[i] == -INFINITY) ? 0.f : fexp<T>(p[i] - m_new);
-      l_part = (i == 0 ? l_part * alpha : l_part) + e;
-      set_frag(pf, i, e);
-    }
-    m_run = m_new;
+    float s[8];
+    mask_scores(st, a.scale, base, lim, pre, qs, g, s);
+    const Frag<T> pf = sm.update(s);
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      o[d][0] *= alpha; o[d][1] *= alpha; o[d][2] *= alpha; o[d][3] *= alpha;
       Frag<T> vf;
       const T* vrow = &Vt[(d * 16 + (lane & 15)) * LDV];
       load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
-      mma32(vf, pf, o[d]);
+      mma32(vf, pf, sm.o[d]);
     }
     __syncthreads();
   }
 
-  // lane holds O[q][d*16 + 4g + e] (unnormalised); total softmax denominator
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  float l_tot = sm.l + __shfl_xor(sm.l, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (blk_b >= blk_e) { m_run = -INFINITY; l_tot = 0.f; }
-
-  if (a.splits > 1) {
-    constexpr int NR = 2 + ND * 4;
-    const int wt = b * gridDim.x + tile;
-    float* P = a.partial + (size_t)wt * a.splits * NR * 256;
-    float* mine = P + (size_t)split * NR * 256;
-    mine[tid] = m_run;
-    mine[256 + tid] = l_tot;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mine[(2 + d * 4 + e) * 256 + tid] = o[d][e];
-    if (!arrive_last(&a.counters[wt], (unsigned)a.splits, tid)) return;
-    float mz = -INFINITY;
-    for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * NR * 256 + tid]);
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_tot = 0.f;
-    for (int z = 0; z < a.splits; ++z) {
-      const float* pz = P + (size_t)z * NR * 256;
-      const float mzz = pz[tid];
-      const float w = (mzz == -INFINITY) ? 0.f : fexp<T>(mzz - mz);
-      l_tot += w * pz[256 + tid];
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[d][e] += w * pz[(2 + d * 4 + e) * 256 + tid];
-    }
-    if (tid == 0) a.counters[wt] = 0u;
-  }
-
   if (!qok) return;
   const float inv = 1.f / l_tot;
   T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(o[d][e] * inv);
+    for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(sm.o[d][e] * inv);
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(512) void attn_small_kernel(AttnArgs a) {
+  constexpr int KB = 32, NW = 8;
+  constexpr int NC = DH / 32, ND = DH / 16;
+  constexpr int NR = 2 + ND * 4;  // floats per lane in the merge buffer
+  __shared__ float red[NW * 64 * NR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int nq = a.nh * a.S;
+  const int qi = tile * 16 + (lane & 15);
+  const bool qok = qi < nq;
+  const int qs = qok ? qi / a.nh : 0, qn = qok ? qi - qs * a.nh : 0;
+
+  int valid = a.desc->valid[b];
+  valid = valid < 0 ? 0 : (valid > a.L ? a.L : valid);
+  const T* __restrict__ qk = reinterpret_cast<const T*>(a.qk);
+  const T* Kp = reinterpret_cast<const T*>(a.desc->kv) + a.kv_k_off + (size_t)b * a.L * DH;
+  const T* Vtp = reinterpret_cast<const T*>(a.vtp) + (size_t)b * DH * a.Lp;
+  const T* Vts = reinterpret_cast<const T*>(a.vts) + (size_t)b * DH * a.Sp;
+  const T* Sq = qk + (size_t)b * a.S * a.ldqk;
+
+  Frag<T> qf[NC];
+  {
+    const T* qrow = Sq + (size_t)qs * a.ldqk + qn * DH;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (qok) load8(qf[c], qrow + c * 32 + g * 8);
+      else
+#pragma unroll
+        for (int i = 0; i < 8; ++i) set_frag(qf[c], i, 0.f);
+    }
+  }
+  const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
+  SoftmaxState<T, DH> sm;
+  sm.init();
+
+  for (int blk = wave; blk < nb_pre + nb_suf; blk += NW) {
+    const bool pre = blk < nb_pre;
+    const int base = pre ? blk * KB : (blk - nb_pre) * KB;
+    const int lim = pre ? valid : a.S;
+    f32x4 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = base + kt * 16 + (lane & 15);
+      const bool kok = key < lim;
+      const T* krow = pre ? Kp + (size_t)key * DH : Sq + (size_t)key * a.ldqk + a.col_k;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        Frag<T> kf;
+        if (kok) load8(kf, krow + c * 32 + g * 8);
+        else
+#pragma unroll
+          for (int i = 0; i < 8; ++i) set_frag(kf, i, 0.f);
+        mma32(kf, qf[c], st[kt]);
+      }
+    }
+    float s[8];
+    mask_scores(st, a.scale, base, lim, pre, qs, g, s);
+    const Frag<T> pf = sm.update(s);
+    const T* vbase = pre ? Vtp + base : Vts + base;
+    const int vld = pre ? a.Lp : a.Sp;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      Frag<T> vf;
+      const T* vrow = vbase + (size_t)(d * 16 + (lane & 15)) * vld;
+      load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
+      mma32(vf, pf, sm.o[d]);
+    }
+  }
+
+  // merge the 8 waves' states: lane layout (q = lane % 16, g = lane / 16), O^T element d*16 + 4g + e
+  float* mine = red + (wave * 64 + lane) * NR;
+  mine[0] = sm.m;
+  mine[1] = sm.l;
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mine[2 + d * 4 + e] = sm.o[d][e];
+  __syncthreads();
+  const int ln = tid & 63, q = ln & 15;
+  const int qi2 = tile * 16 + q;
+  if (qi2 >= nq) return;
+  const int qs2 = qi2 / a.nh, qn2 = qi2 - qs2 * a.nh;
+  float mz = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mz = fmaxf(mz, red[(w * 64 + ln) * NR]);
+  float wt[NW], lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float mw = red[(w * 64 + ln) * NR];
+    wt[w] = (mw == -INFINITY) ? 0.f : fexp<T>(mw - mz);
+    float lw = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) lw += red[(w * 64 + gg * 16 + q) * NR + 1];
+    lsum += wt[w] * lw;
+  }
+  const float inv = 1.f / lsum;
+  T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs2) * a.ldo + qn2 * DH;
+  const int g2 = ln >> 4;
+  for (int d = tid >> 6; d < ND; d += NW)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += wt[w] * red[(w * 64 + ln) * NR + 2 + d * 4 + e];
+      orow[d * 16 + g2 * 4 + e] = from_f32<T>(acc * inv);
+    }
+}
+
+// Prefix values, transposed once per call: vt[l][b][d][Lp] = V_l[b][key][d] for
+// keys < valid_len[b], 0 for the rest (padded keys are not read).  32 keys x 64
+// features per block through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const CallDesc* __restrict__ desc, int B, int L, int DH,
+                                                          int Lp, T* __restrict__ vt) {
+  __shared__ T tileb[32][64 + 1];
+  const int k0 = blockIdx.x * 32, d0 = blockIdx.y * 64, lb = blockIdx.z;  // lb = layer * B + b
+  const int layer = lb / B, b = lb - layer * B;
+  int valid = desc->valid[b];
+  valid = valid < 0 ? 0 : (valid > L ? L : valid);
+  const T* src = reinterpret_cast<const T*>(desc->kv) + (((size_t)layer * 2 + 1) * B + b) * (size_t)L * DH;
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int kk = i / 64, dd = i % 64, key = k0 + kk;
+    tileb[kk][dd] = (key < valid && d0 + dd < DH) ? src[(size_t)key * DH + d0 + dd] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  T* dst = vt + ((size_t)lb * DH) * Lp;
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int dd = i / 32, kk = i % 32;
+    if (d0 + dd < DH) dst[(size_t)(d0 + dd) * Lp + k0 + kk] = tileb[kk][dd];
+  }
 }
 
 }  // namespace pi0x

@@ -9,6 +9,8 @@ namespace pi0x {
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// 16 raw bytes as a native vector (HIP's uint4 struct copies through memory)
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 // Per-call arguments that change between calls without re-recording the
 // captured graph.  A one-thread kernel writes this struct on the caller's
@@ -97,28 +99,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k = 0.7978845608028654f;  // sqrt(2 / pi)
-  return 0.5f * x * (1.0f + tanhf(k * (x + 0.044715f * x * x * x)));
-}
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
-// Deterministic split reduction support: a block that finishes its share of a
-// tile bumps the tile's arrival counter; the block that arrives last gets
-// true, sums every share in a fixed order and resets the counter to 0 for the
-// next launch.  Every block of the tile calls it exactly once.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int tid) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    unsigned prev = atomicAdd(counter, 1u);
-    s_last = (prev == expected - 1u);
-  }
-  __syncthreads();
-  if (!s_last) return false;
-  __threadfence();
-  return true;
+// tanh-GELU through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)):
+// gelu(x) = x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3))).  The bf16 path
+// uses the hardware exp2, the float32 path libm expf.
+template <typename T>
+__device__ __forceinline__ float gelu_tanh_fast(float x) {
+  const float u = -1.5957691216057308f * (x + 0.044715f * x * x * x);  // -2 sqrt(2/pi) (...)
+  return x / (1.0f + (sizeof(T) == 2 ? __expf(u) : expf(u)));
 }
 
 }  // namespace pi0x

@@ -1,22 +1,40 @@
 // pi0x runtime: the C ABI of include/pi0x.h on top of the gfx950 kernels.
 //
 // create() repacks the nn.Linear-layout weight blob into the layouts the
-// kernels want (q/k rows paired for rotate-half RoPE, gate/up interleaved in
-// blocks of 16, the time half of action_time_mlp_in split off), converts it to
-// the model dtype and uploads it; it also builds the float32 rotary table on
-// the device and allocates every workspace for the handle's capacity.
+// kernels want and uploads it:
+//  * q/k rows of every head paired for rotate-half RoPE (stored row block 2p =
+//    head elements 16p.., block 2p+1 = half+16p..), v rows after them;
+//  * gate/up rows interleaved in blocks of 16 (block 2p = gate rows 16p..,
+//    block 2p+1 = up rows 16p..);
+//  * the Gemma norm scales (1 + w) of the input and post-attention norms folded
+//    into the columns of the q/k/v and gate/up weights (the kernels apply the
+//    1/rms row factor in the GEMM epilogue);
+//  * action_time_mlp_in split into its time half (a GEMM once per call for
+//    every step's time features) and its action half, which is multiplied
+//    into action_in_proj (both linear) to a width x action_dim matrix;
+//  * action_out_proj with the final norm's (1 + w) folded into its columns.
+// It also builds the float32 rotary table on the device and allocates every
+// workspace for the handle's capacity.
 //
-// A call writes a small device descriptor with its pointers and replays the
-// hipGraph recorded for (batch, prefix length, steps, mode); the graph is
-// recorded on first use, so later calls with new buffers or new valid lengths
-// replay it unchanged.
+// One Euler step is 3 + 5 * depth kernels: the first layer of the time MLP
+// (plus the state token copy), action_time_mlp_out (writes the action rows of
+// the residual stream), per layer [q/k/v + RoPE, attention, o_proj + residual,
+// gate/up + GeGLU, down + residual], and action_out_proj + Euler update (the
+// final norm's 1/rms applied as a row scale).  Once per call: the time
+// features of every step, the time half of action_time_mlp_in for every step,
+// the transpose of the prefix values and the state tokens.  A call writes a small device descriptor with its pointers and
+// replays the hipGraph recorded for (batch, prefix length, steps, mode); the
+// graph is recorded on first use, so later calls with new buffers or new
+// valid lengths replay it unchanged.
 #include "pi0x.h"
 
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "attention.h"
@@ -35,29 +53,27 @@ pi0x_status fail(pi0x_status s, const std::string& msg) {
   return s;
 }
 
-#define PI0X_HIP(x)                                                                      \
-  do {                                                                                   \
-    hipError_t e_ = (x);                                                                 \
+#define PI0X_HIP(x)                                                                                 \
+  do {                                                                                              \
+    hipError_t e_ = (x);                                                                            \
     if (e_ != hipSuccess) return fail(PI0X_ERR_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
-#define PI0X_TRY(x)                         \
-  do {                                      \
-    pi0x_status s_ = (x);                   \
-    if (s_ != PI0X_OK) return s_;           \
+#define PI0X_TRY(x)               \
+  do {                            \
+    pi0x_status s_ = (x);         \
+    if (s_ != PI0X_OK) return s_; \
   } while (0)
 
 constexpr int kMaxGraphs = 32;
-constexpr size_t kGemmPartialFloats = (size_t)16 << 20;  // 64 MiB of split-K partial tiles
+constexpr size_t kGemmPartialFloats = (size_t)16 << 20;  // split-K partial tiles (float32 path)
 constexpr int kCounters = 1 << 16;
 
 struct Layer {
-  void* wqkv;   // [(H+2)*D][W], q/k rows paired for RoPE
+  void* wqkv;   // [(H+2)*D][W], q/k rows paired for RoPE, columns scaled by (1 + input_norm)
   void* wo;     // [W][H*D]
-  void* wgu;    // [2M][W], gate/up interleaved by 16 rows
+  void* wgu;    // [2M][W], gate/up interleaved by 16 rows, columns scaled by (1 + post_norm)
   void* wdown;  // [W][M]
-  float* in1p;  // 1 + input_norm
-  float* post1p;
 };
 
 struct Key {
@@ -73,31 +89,43 @@ uint16_t host_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
 }  // namespace
 
 struct pi0x_expert {
   pi0x_config cfg;
   int device = 0;
   int esz = 4;
-  int W, D, M, nh, dh, H, A, Sd, S, qd, nqkv, Bmax, Lmax;
+  int W, D, M, nh, dh, H, A, Sd, S, qd, nqkv, Bmax, Lmax, Lpmax, Sp;
   std::vector<void*> allocs;
   std::vector<Layer> layers;
-  float* final1p = nullptr;
-  void *w_ta = nullptr, *w_tt = nullptr, *w_mo = nullptr;
-  float *b_mi = nullptr, *b_mo = nullptr, *w_in = nullptr, *b_in = nullptr, *w_s = nullptr, *b_s = nullptr;
-  float *w_out = nullptr, *b_out = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
-  float* hbuf = nullptr;
-  void *y = nullptr, *qkv = nullptr, *o = nullptr, *gbuf = nullptr, *ain = nullptr, *u = nullptr, *tau = nullptr;
+  void *w_tt = nullptr, *w_mo = nullptr;  // time half of action_time_mlp_in, action_time_mlp_out
+  float* w_comb = nullptr;  // [W][A] action half of action_time_mlp_in times action_in_proj
+  void* w_outp = nullptr;   // [Apad][W] action_out_proj, columns scaled by (1 + final_norm), rows >= A zero
+  int Apad = 0;
+  float *b_mi = nullptr, *b_mo = nullptr, *w_s = nullptr, *b_s = nullptr, *b_out = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  float* hs = nullptr;  // state tokens of the call [B][W]
+  float* hbuf = nullptr;  // residual stream [R][W] float32
+  void* hb = nullptr;     // bf16 copy of the residual stream (bf16 mode)
+  float* ssq = nullptr;   // per-row sum-of-squares partials of the residual stream [R][W/16]
+  void *qk = nullptr, *o = nullptr, *gbuf = nullptr, *u = nullptr, *tau = nullptr;
+  void *vts = nullptr, *vtp = nullptr;  // suffix / prefix values, transposed
   float *x = nullptr, *tbias = nullptr;
   float* gemm_partial = nullptr;
   unsigned* gemm_counters = nullptr;
-  float* attn_partial = nullptr;
-  size_t attn_partial_floats = 0;
-  unsigned* attn_counters = nullptr;
   CallDesc* desc = nullptr;
   hipStream_t cap_stream = nullptr;
   std::map<Key, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
   std::vector<Key> graph_order;
+  // kernel timing (pi0x_set_timing): event pairs recorded around launches
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<std::pair<int, size_t>> ev_marks;  // (kernel class, index of the start event)
+
+  bool bf16() const { return cfg.dtype == PI0X_BF16; }
 
   pi0x_status alloc(void** p, size_t bytes) {
     *p = nullptr;
@@ -122,13 +150,90 @@ struct pi0x_expert {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Launch helpers
+// Kernel timing: while enabled, calls run eagerly and every launch of a
+// tracked kernel class is bracketed by a pair of HIP events on its stream.
 // ---------------------------------------------------------------------------
+pi0x_status next_event(pi0x_expert* h, hipEvent_t* e) {
+  if (h->ev_used == h->ev_pool.size()) {
+    hipEvent_t ev;
+    PI0X_HIP(hipEventCreate(&ev));
+    h->ev_pool.push_back(ev);
+  }
+  *e = h->ev_pool[h->ev_used++];
+  return PI0X_OK;
+}
+
+struct Timed {
+  pi0x_expert* h;
+  hipStream_t s;
+  int cls;
+  size_t start = 0;
+  bool on;
+  pi0x_status st = PI0X_OK;
+  Timed(pi0x_expert* h_, hipStream_t s_, int c) : h(h_), s(s_), cls(c), on(h_->timing) {
+    if (!on) return;
+    hipEvent_t e;
+    st = next_event(h, &e);
+    if (st == PI0X_OK && hipEventRecord(e, s) != hipSuccess) st = fail(PI0X_ERR_HIP, "hipEventRecord failed");
+    start = h->ev_used - 1;
+  }
+  pi0x_status done() {
+    if (!on || st != PI0X_OK) return st;
+    hipEvent_t e;
+    PI0X_TRY(next_event(h, &e));
+    PI0X_HIP(hipEventRecord(e, s));
+    h->ev_marks.push_back({cls, start});
+    return PI0X_OK;
+  }
+};
+
+#define PI0X_TIMED(cls, call) \
+  do {                        \
+    Timed t_(h, s, (cls));    \
+    PI0X_TRY(t_.st);          \
+    PI0X_TRY(call);           \
+    PI0X_TRY(t_.done());      \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// GEMM dispatch
+// ---------------------------------------------------------------------------
+// Column-group width of the sum-of-squares partials a residual producer writes
+// for M rows (the wave or block width of the kernel launch_gemm picks for it).
+int producer_group(bool bf16, int M) {
+  if (bf16) return M <= 64 ? 16 : 64;
+  return M <= 1024 ? 32 : 64;
+}
+
+struct NormIn {
+  const float* ssq = nullptr;
+  int np = 0;
+};
+
+GemmArgs make_args(pi0x_expert* h, const void* A, int lda, const void* W, int M, int N, int K, NormIn nin) {
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.W = W;
+  g.ldw = K;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.splits = 1;
+  g.partial = h->gemm_partial;
+  g.counters = h->gemm_counters;
+  g.ssq_in = nin.ssq;
+  g.ssq_np = nin.np;
+  g.norm_dim = h->W;
+  g.norm_eps = h->cfg.rms_eps;
+  return g;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
-pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, const void* A, int lda, const void* W, int M, int N,
-                            int K, const Epi& epi) {
-  const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  const int KI = K / 32;
+pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi& epi) {
+  (void)h;
+  const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
+  const int KI = g.K / 32;
   int splits = 1;
   if (tiles < 160) {
     splits = (256 + tiles - 1) / tiles;
@@ -138,43 +243,91 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, const void* A, int ld
     while (splits > 1 && (size_t)tiles * splits * BM * BN > kGemmPartialFloats) --splits;
     if (tiles > kCounters) splits = 1;
   }
-  GemmArgs g{A, lda, W, K, M, N, K, splits, h->gemm_partial, h->gemm_counters};
-  dim3 grid(N / BN, (M + BM - 1) / BM, splits);
+  g.splits = splits;
+  dim3 grid(g.N / BN, (g.M + BM - 1) / BM, splits);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, Epi>), grid, dim3(256), 0, s, g, epi);
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
 }
 
-template <typename T, class Epi>
-pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, const void* W, int M, int N, int K,
-                        const Epi& epi) {
-  if (M <= 0) return PI0X_OK;
-  if (K % 32 != 0 || N % 32 != 0) return fail(PI0X_ERR_SHAPE, "GEMM dims must be multiples of 32");
-  if (M > 1024 && N % 128 == 0) return launch_gemm_cfg<T, 128, 128, 2, 2>(h, s, A, lda, W, M, N, K, epi);
-  if (M > 64 && N % 64 == 0) return launch_gemm_cfg<T, 128, 64, 2, 2>(h, s, A, lda, W, M, N, K, epi);
-  return launch_gemm_cfg<T, 64, 32, 4, 1>(h, s, A, lda, W, M, N, K, epi);
+template <int BM, int BN, class Epi>
+pi0x_status launch_gemm_big(hipStream_t s, GemmArgs g, const Epi& epi) {
+  dim3 grid(g.N / BN, (g.M + BM - 1) / BM, 1);
+  constexpr size_t smem = big_smem_bytes<BM, BN>();
+  gemm_big_kernel<BM, BN, Epi><<<grid, dim3(256), smem, s>>>(g, epi);
+  PI0X_HIP(hipGetLastError());
+  return PI0X_OK;
 }
 
+template <int BN, class Epi>
+pi0x_status launch_gemm_skinny(hipStream_t s, GemmArgs g, const Epi& epi) {
+  hipLaunchKernelGGL((gemm_skinny_kernel<BN, Epi>), dim3(g.N / BN), dim3(512), 0, s, g, epi);
+  PI0X_HIP(hipGetLastError());
+  return PI0X_OK;
+}
+
+// The residual producers (kSsq) use the kernel whose column group matches
+// producer_group(); the other GEMMs pick their tiling for parallelism.
+template <typename T, class Epi>
+pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, const void* W, int M, int N, int K,
+                        const Epi& epi, NormIn nin = NormIn()) {
+  if (M <= 0) return PI0X_OK;
+  if (K % 64 != 0 || N % 64 != 0) return fail(PI0X_ERR_SHAPE, "GEMM dims must be multiples of 64");
+  const GemmArgs g = make_args(h, A, lda, W, M, N, K, nin);
+  if constexpr (sizeof(T) == 2) {
+    if (M <= 64) {
+      if constexpr (Epi::kSsq) {
+        return launch_gemm_skinny<16>(s, g, epi);
+      } else if constexpr (Epi::kPaired) {
+        return N / 64 >= 128 ? launch_gemm_skinny<64>(s, g, epi) : launch_gemm_skinny<32>(s, g, epi);
+      } else {
+        return N / 32 >= 128 ? launch_gemm_skinny<32>(s, g, epi) : launch_gemm_skinny<16>(s, g, epi);
+      }
+    }
+    if (N % 128 == 0) return launch_gemm_big<128, 128>(s, g, epi);
+    return fail(PI0X_ERR_SHAPE, "bf16 GEMM with more than 64 rows needs N % 128 == 0");
+  } else {
+    if (M > 1024 && N % 128 == 0) return launch_gemm_cfg<T, 128, 128, 2, 2>(h, s, g, epi);
+    if (M > 64) return launch_gemm_cfg<T, 128, 64, 2, 2>(h, s, g, epi);
+    return launch_gemm_cfg<T, 64, 32, 4, 1>(h, s, g, epi);
+  }
+}
+
+// Kernels that take more than 64 KiB of dynamic LDS must opt in once.
+template <class Epi>
+pi0x_status allow_big_smem() {
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_big_kernel<128, 128, Epi>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)big_smem_bytes<128, 128>()));
+  return PI0X_OK;
+}
+
+pi0x_status allow_big_smem_all() {
+  PI0X_TRY(allow_big_smem<EpiStore<float>>());
+  PI0X_TRY(allow_big_smem<EpiStore<bf16>>());
+  PI0X_TRY(allow_big_smem<EpiSuffixRows<bf16>>());
+  PI0X_TRY(allow_big_smem<EpiResidual<bf16>>());
+  PI0X_TRY(allow_big_smem<EpiQkvRope<bf16>>());
+  PI0X_TRY(allow_big_smem<EpiGeglu<bf16>>());
+  PI0X_TRY(allow_big_smem<EpiEuler>());
+  return PI0X_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Attention dispatch
+// ---------------------------------------------------------------------------
 template <typename T, int DH>
 pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer) {
-  const int ntiles = (h->nh * h->S + 63) / 64;
-  const int wgs = B * ntiles;
-  int splits = 1;
-  if (wgs < 128) {
-    splits = (256 + wgs - 1) / wgs;
-    if (splits > 32) splits = 32;
-  }
-  const size_t per = (size_t)(2 + DH / 4) * 256;
-  while (splits > 1 && (size_t)wgs * splits * per > h->attn_partial_floats) --splits;
-  if (wgs > kCounters) splits = 1;
+  const int Lp = round_up(L > 0 ? L : 1, 32);
   AttnArgs a;
-  a.qkv = h->qkv;
-  a.ldqkv = h->nqkv;
+  a.qk = h->qk;
+  a.ldqk = h->qd + DH;
   a.col_k = h->qd;
-  a.col_v = h->qd + h->dh;
   a.desc = h->desc;
   a.kv_k_off = ((size_t)layer * 2 + 0) * B * L * DH;
-  a.kv_v_off = ((size_t)layer * 2 + 1) * B * L * DH;
+  a.vtp = reinterpret_cast<const T*>(h->vtp) + (size_t)layer * B * DH * Lp;
+  a.Lp = Lp;
+  a.vts = h->vts;
+  a.Sp = h->Sp;
   a.B = B;
   a.L = L;
   a.S = h->S;
@@ -182,10 +335,12 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   a.out = h->o;
   a.ldo = h->qd;
   a.scale = 1.0f / std::sqrt((float)DH);
-  a.splits = splits;
-  a.partial = h->attn_partial;
-  a.counters = h->attn_counters;
-  hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(ntiles, B, splits), dim3(256), 0, s, a);
+  const int nq = h->nh * h->S;
+  if (B * ((nq + 63) / 64) >= 128) {
+    hipLaunchKernelGGL((attn_kernel<T, DH>), dim3((nq + 63) / 64, B), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_small_kernel<T, DH>), dim3((nq + 15) / 16, B), dim3(512), 0, s, a);
+  }
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
 }
@@ -201,45 +356,85 @@ pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer) 
   return fail(PI0X_ERR_SHAPE, "unsupported head_dim");
 }
 
-// The whole loop: N > 0 is the N-step sampler, N == 0 one velocity evaluation.
+template <typename T>
+pi0x_status launch_transpose_v(pi0x_expert* h, hipStream_t s, int B, int L) {
+  if (L <= 0) return PI0X_OK;
+  const int Lp = round_up(L, 32);
+  hipLaunchKernelGGL((transpose_v_kernel<T>), dim3(Lp / 32, (h->dh + 63) / 64, h->D * B), dim3(256), 0, s, h->desc, B,
+                     L, h->dh, Lp, reinterpret_cast<T*>(h->vtp));
+  PI0X_HIP(hipGetLastError());
+  return PI0X_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The loop: N > 0 is the N-step sampler, N == 0 one velocity evaluation.
+// ---------------------------------------------------------------------------
 template <typename T>
 pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
   const int W = h->W, S = h->S, H = h->H, R = B * S, AR = B * H;
   const int steps = N > 0 ? N : 1;
   const float eps = h->cfg.rms_eps;
   const float dt = N > 0 ? (float)(-1.0 / (double)N) : 0.f;
-  hipLaunchKernelGGL((time_features_kernel<T>), dim3(steps), dim3(256), 0, s, h->desc, N, W,
-                     (double)h->cfg.time_min_period, (double)h->cfg.time_max_period, (T*)h->tau);
-  PI0X_HIP(hipGetLastError());
+  const bool bf = h->bf16();
+  T* hb = bf ? reinterpret_cast<T*>(h->hb) : nullptr;
+  // A operand of the norm-consuming projections: the residual stream itself
+  // (its bf16 copy in bf16 mode)
+  const void* hA = bf ? h->hb : (const void*)h->hbuf;
+  // sum-of-squares partials: one per (row, producer column group)
+  const int G = producer_group(bf, R);
+  if (producer_group(bf, AR) != G) return fail(PI0X_ERR_SHAPE, "inconsistent residual producer tiling");
+  const int np = W / G;
+  const NormIn nin{h->ssq, np};
+
+  auto time_feats = [&]() -> pi0x_status {
+    hipLaunchKernelGGL((time_features_kernel<T>), dim3(steps), dim3(256), 0, s, h->desc, N, W,
+                       (double)h->cfg.time_min_period, (double)h->cfg.time_max_period, (T*)h->tau);
+    PI0X_HIP(hipGetLastError());
+    return PI0X_OK;
+  };
+  PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, time_feats());
   // time half of action_time_mlp_in (+ its bias) for every evaluated time
-  PI0X_TRY(launch_gemm<T>(h, s, h->tau, W, h->w_tt, steps, W, W, EpiStore<float>{h->tbias, W, h->b_mi, 0}));
+  PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
+             (launch_gemm<T>(h, s, h->tau, W, h->w_tt, steps, W, W, EpiStore<float>{h->tbias, W, h->b_mi, 0})));
+  PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_transpose_v<T>(h, s, B, L));
+  auto state_tok = [&]() -> pi0x_status {
+    hipLaunchKernelGGL(state_token_kernel, dim3(B), dim3(256), 0, s, h->desc, h->Sd, W, h->w_s, h->b_s, h->hs);
+    PI0X_HIP(hipGetLastError());
+    return PI0X_OK;
+  };
+  PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, state_tok());
+  const int nA = (AR + 15) / 16;
   for (int k = 0; k < steps; ++k) {
     const int first = (k == 0);
-    hipLaunchKernelGGL((embed_inputs_kernel<T>), dim3(AR + B), dim3(256), 0, s, h->desc, h->x, first, B, H, h->A,
-                       h->Sd, W, S, h->w_in, h->b_in, h->w_s, h->b_s, (T*)h->ain, h->hbuf, W);
-    PI0X_HIP(hipGetLastError());
-    PI0X_TRY(launch_gemm<T>(h, s, h->ain, W, h->w_ta, AR, W, W, EpiStore<T>{(T*)h->u, W, h->tbias + (size_t)k * W, 1}));
-    PI0X_TRY(launch_gemm<T>(h, s, h->u, W, h->w_mo, AR, W, W, EpiSuffixRows{h->hbuf, W, H, S, h->b_mo}));
+    auto suffix_in = [&]() -> pi0x_status {
+      hipLaunchKernelGGL((suffix_in_kernel<T>), dim3(nA + B), dim3(256), 0, s, h->desc, h->x, first, AR, nA, h->A, W,
+                         S, h->w_comb, h->tbias + (size_t)k * W, (T*)h->u, h->hs, h->hbuf, hb, h->ssq, G);
+      PI0X_HIP(hipGetLastError());
+      return PI0X_OK;
+    };
+    PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, suffix_in());
+    PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
+               (launch_gemm<T>(h, s, h->u, W, h->w_mo, AR, W, W,
+                               EpiSuffixRows<T>{h->hbuf, hb, W, H, S, h->b_mo, h->ssq, np})));
     for (int l = 0; l < h->D; ++l) {
       const Layer& ly = h->layers[l];
-      hipLaunchKernelGGL((rmsnorm_kernel<T>), dim3((R + 3) / 4), dim3(256), 0, s, h->hbuf, W, ly.in1p, (T*)h->y, W,
-                         R, W, eps);
-      PI0X_HIP(hipGetLastError());
-      PI0X_TRY(launch_gemm<T>(h, s, h->y, W, ly.wqkv, R, h->nqkv, W,
-                              EpiQkvRope<T>{(T*)h->qkv, h->nqkv, h->qd + h->dh, h->dh, S, L, h->desc, h->rope_cos,
-                                            h->rope_sin}));
-      PI0X_TRY(launch_attn<T>(h, s, B, L, l));
-      PI0X_TRY(launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd, EpiResidual{h->hbuf, W}));
-      hipLaunchKernelGGL((rmsnorm_kernel<T>), dim3((R + 3) / 4), dim3(256), 0, s, h->hbuf, W, ly.post1p, (T*)h->y,
-                         W, R, W, eps);
-      PI0X_HIP(hipGetLastError());
-      PI0X_TRY(launch_gemm<T>(h, s, h->y, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}));
-      PI0X_TRY(launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M, EpiResidual{h->hbuf, W}));
+      PI0X_TIMED(PI0X_KERNEL_QKV_ROPE,
+                 (launch_gemm<T>(h, s, hA, W, ly.wqkv, R, h->nqkv, W,
+                                 EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, L, h->desc,
+                                               h->rope_cos, h->rope_sin, (T*)h->vts, h->Sp},
+                                 nin)));
+      PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l));
+      PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
+                                                     EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+      PI0X_TIMED(PI0X_KERNEL_GATE_UP,
+                 (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin)));
+      PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M,
+                                                   EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
     }
     const int last = (k == steps - 1);
-    hipLaunchKernelGGL(final_kernel, dim3((AR + 3) / 4), dim3(256), 0, s, h->desc, h->hbuf, W, h->final1p, h->w_out,
-                       h->b_out, h->x, first, last, N > 0 ? 0 : 1, dt, AR, H, S, W, h->A, eps);
-    PI0X_HIP(hipGetLastError());
+    PI0X_TIMED(PI0X_KERNEL_FINAL,
+               (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W,
+                               EpiEuler{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1, dt}, nin)));
   }
   return PI0X_OK;
 }
@@ -247,9 +442,9 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
 pi0x_status run(pi0x_expert* h, int B, int L, int N, hipStream_t stream) {
   const Key key{B, L, N, N > 0 ? 0 : 1};
   auto launch_eager = [&](hipStream_t s) -> pi0x_status {
-    return h->cfg.dtype == PI0X_BF16 ? enqueue<bf16>(h, s, B, L, N) : enqueue<float>(h, s, B, L, N);
+    return h->bf16() ? enqueue<bf16>(h, s, B, L, N) : enqueue<float>(h, s, B, L, N);
   };
-  if (!h->cfg.use_graphs) return launch_eager(stream);
+  if (!h->cfg.use_graphs || h->timing) return launch_eager(stream);
   auto it = h->graphs.find(key);
   if (it == h->graphs.end()) {
     if ((int)h->graphs.size() >= kMaxGraphs) {
@@ -295,22 +490,24 @@ pi0x_status check_config(const pi0x_config* c) {
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return fail(PI0X_ERR_SHAPE, "head_dim must be 32, 64, 128 or 256");
   if (c->width % 256 != 0) return fail(PI0X_ERR_SHAPE, "width must be a multiple of 256");
-  if (c->mlp_dim % 64 != 0) return fail(PI0X_ERR_SHAPE, "mlp_dim must be a multiple of 64");
-  if ((c->num_heads * c->head_dim) % 64 != 0) return fail(PI0X_ERR_SHAPE, "num_heads*head_dim must be a multiple of 64");
+  if (c->mlp_dim % 128 != 0) return fail(PI0X_ERR_SHAPE, "mlp_dim must be a multiple of 128");
+  if ((c->num_heads * c->head_dim) % 128 != 0)
+    return fail(PI0X_ERR_SHAPE, "num_heads*head_dim must be a multiple of 128");
   if (c->action_dim > 64 || c->state_dim > 64) return fail(PI0X_ERR_SHAPE, "action_dim and state_dim must be <= 64");
   if ((long)c->max_batch * (c->action_horizon + 1) > (1L << 24)) return fail(PI0X_ERR_CAPACITY, "max_batch too large");
   return PI0X_OK;
 }
 
 size_t weight_count(const pi0x_config* c) {
-  const size_t W = c->width, M = c->mlp_dim, qd = (size_t)c->num_heads * c->head_dim, kd = (size_t)c->num_kv_heads * c->head_dim;
+  const size_t W = c->width, M = c->mlp_dim, qd = (size_t)c->num_heads * c->head_dim,
+               kd = (size_t)c->num_kv_heads * c->head_dim;
   const size_t A = c->action_dim, Sd = c->state_dim;
   const size_t layer = W + qd * W + 2 * kd * W + W * qd + W + 3 * M * W;
   return layer * c->depth + W + (W * Sd + W) + (W * A + W) + (W * 2 * W + W) + (W * W + W) + (A * W + A);
 }
 
-template <typename T>
-void put(std::vector<T>& dst, size_t i, float v);
+template <typename E>
+void put(std::vector<E>& dst, size_t i, float v);
 template <>
 void put<float>(std::vector<float>& dst, size_t i, float v) { dst[i] = v; }
 template <>
@@ -325,13 +522,13 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
     PI0X_HIP(hipMemcpy(*dst, v.data(), v.size() * sizeof(E), hipMemcpyHostToDevice));
     return PI0X_OK;
   };
-  auto upf = [&](float** dst, const float* src, size_t n, bool one_plus) -> pi0x_status {
-    std::vector<float> v(src, src + n);
-    if (one_plus)
-      for (auto& x : v) x = 1.0f + x;
-    PI0X_TRY(h->allocT(dst, n * sizeof(float)));
-    PI0X_HIP(hipMemcpy(*dst, v.data(), n * sizeof(float), hipMemcpyHostToDevice));
-    return PI0X_OK;
+  // value in the model dtype, as float (bf16 mode: the blob value rounded to bf16)
+  auto md = [&](float x) -> float {
+    if (!h->bf16()) return x;
+    uint32_t u = (uint32_t)host_bf16(x) << 16;
+    float r;
+    std::memcpy(&r, &u, 4);
+    return r;
   };
   h->layers.resize(h->D);
   for (int l = 0; l < h->D; ++l) {
@@ -346,7 +543,11 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
     const float* wu = wg + (size_t)M * W;
     const float* wd = wu + (size_t)M * W;
     Layer& ly = h->layers[l];
-    // q/k/v with q and k rows paired for rotate-half RoPE
+    std::vector<float> s_in(W), s_post(W);
+    for (int k = 0; k < W; ++k) {
+      s_in[k] = 1.0f + md(in_norm[k]);
+      s_post[k] = 1.0f + md(post[k]);
+    }
     {
       const int rows = qd + 2 * dh;
       std::vector<E> v((size_t)rows * W);
@@ -359,7 +560,7 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
         } else {
           src = wv + (size_t)(c - qd - dh) * W;
         }
-        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, src[k]);
+        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, md(src[k]) * s_in[k]);
       }
       PI0X_TRY(up(&ly.wqkv, v));
     }
@@ -373,7 +574,7 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
       for (int c = 0; c < 2 * M; ++c) {
         const int pblk = c / 32, sel = (c % 32) / 16, e = c % 16;
         const float* src = (sel == 0 ? wg : wu) + ((size_t)pblk * 16 + e) * W;
-        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, src[k]);
+        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, md(src[k]) * s_post[k]);
       }
       PI0X_TRY(up(&ly.wgu, v));
     }
@@ -382,8 +583,6 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
       for (size_t i = 0; i < v.size(); ++i) put<E>(v, i, wd[i]);
       PI0X_TRY(up(&ly.wdown, v));
     }
-    PI0X_TRY(upf(&ly.in1p, in_norm, W, true));
-    PI0X_TRY(upf(&ly.post1p, post, W, true));
   }
   const float* p = blob + (size_t)h->D * layer_sz;
   const float* final_norm = p;
@@ -397,75 +596,102 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
   const float* bmo = wmo + (size_t)W * W;
   const float* wout = bmo + W;
   const float* bout = wout + (size_t)h->A * W;
-  PI0X_TRY(upf(&h->final1p, final_norm, W, true));
+  const int A = h->A;
   {
-    std::vector<E> va((size_t)W * W), vt((size_t)W * W), vo((size_t)W * W);
+    std::vector<E> vt((size_t)W * W), vo((size_t)W * W);
     for (int r = 0; r < W; ++r)
       for (int k = 0; k < W; ++k) {
-        put<E>(va, (size_t)r * W + k, wmi[(size_t)r * 2 * W + k]);
         put<E>(vt, (size_t)r * W + k, wmi[(size_t)r * 2 * W + W + k]);
         put<E>(vo, (size_t)r * W + k, wmo[(size_t)r * W + k]);
       }
-    PI0X_TRY(up(&h->w_ta, va));
     PI0X_TRY(up(&h->w_tt, vt));
     PI0X_TRY(up(&h->w_mo, vo));
   }
-  // small head matrices and every bias stay float32 (bf16 mode: the blob's
+  // action_in_proj folded into the action half of action_time_mlp_in:
+  // W_mi,a (W_in x + b_in) = (W_mi,a W_in) x + W_mi,a b_in, products in double
+  {
+    std::vector<float> comb((size_t)W * A), bmi2(W);
+    std::vector<double> win((size_t)W * A), bin(W);
+    for (size_t i = 0; i < win.size(); ++i) win[i] = md(wi[i]);
+    for (int k = 0; k < W; ++k) bin[k] = md(bi[k]);
+    std::vector<double> acc(A);
+    for (int o = 0; o < W; ++o) {
+      std::fill(acc.begin(), acc.end(), 0.0);
+      double bacc = md(bmi[o]);
+      const float* wr = wmi + (size_t)o * 2 * W;
+      for (int k = 0; k < W; ++k) {
+        const double wk = md(wr[k]);
+        const double* wik = &win[(size_t)k * A];
+        for (int a = 0; a < A; ++a) acc[a] += wk * wik[a];
+        bacc += wk * bin[k];
+      }
+      for (int a = 0; a < A; ++a) comb[(size_t)o * A + a] = (float)acc[a];
+      bmi2[o] = (float)bacc;
+    }
+    PI0X_TRY(h->allocT(&h->w_comb, comb.size() * sizeof(float)));
+    PI0X_HIP(hipMemcpy(h->w_comb, comb.data(), comb.size() * sizeof(float), hipMemcpyHostToDevice));
+    PI0X_TRY(h->allocT(&h->b_mi, W * sizeof(float)));
+    PI0X_HIP(hipMemcpy(h->b_mi, bmi2.data(), W * sizeof(float), hipMemcpyHostToDevice));
+  }
+  // action_out_proj with the final norm's (1 + w) folded into its columns,
+  // padded with zero rows to a multiple of 128 outputs
+  {
+    h->Apad = round_up(A, 128);
+    std::vector<E> v((size_t)h->Apad * W);
+    for (int r = 0; r < h->Apad; ++r)
+      for (int k = 0; k < W; ++k)
+        put<E>(v, (size_t)r * W + k, r < A ? md(wout[(size_t)r * W + k]) * (1.0f + md(final_norm[k])) : 0.f);
+    PI0X_TRY(up(&h->w_outp, v));
+  }
+  // state_proj and the remaining biases stay float32 (bf16 mode: the blob's
   // values rounded to bf16, held exactly in float32)
   auto small = [&](float** dst, const float* src, size_t n) -> pi0x_status {
-    std::vector<float> v(src, src + n);
-    if (h->cfg.dtype == PI0X_BF16)
-      for (auto& x : v) {
-        uint32_t u = (uint32_t)host_bf16(x) << 16;
-        std::memcpy(&x, &u, 4);
-      }
+    std::vector<float> v(n);
+    for (size_t i = 0; i < n; ++i) v[i] = md(src[i]);
     PI0X_TRY(h->allocT(dst, n * sizeof(float)));
     PI0X_HIP(hipMemcpy(*dst, v.data(), n * sizeof(float), hipMemcpyHostToDevice));
     return PI0X_OK;
   };
-  PI0X_TRY(small(&h->b_mi, bmi, W));
   PI0X_TRY(small(&h->b_mo, bmo, W));
-  PI0X_TRY(small(&h->w_in, wi, (size_t)W * h->A));
-  PI0X_TRY(small(&h->b_in, bi, W));
   PI0X_TRY(small(&h->w_s, ws, (size_t)W * h->Sd));
   PI0X_TRY(small(&h->b_s, bs, W));
-  PI0X_TRY(small(&h->w_out, wout, (size_t)h->A * W));
-  PI0X_TRY(small(&h->b_out, bout, h->A));
+  PI0X_TRY(small(&h->b_out, bout, A));
   return PI0X_OK;
 }
 
-pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, size_t weights_bytes, pi0x_expert* h) {
+pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_expert* h) {
   h->cfg = *cfg;
   PI0X_HIP(hipGetDevice(&h->device));
   h->esz = cfg->dtype == PI0X_BF16 ? 2 : 4;
   h->W = cfg->width; h->D = cfg->depth; h->M = cfg->mlp_dim; h->nh = cfg->num_heads; h->dh = cfg->head_dim;
   h->H = cfg->action_horizon; h->A = cfg->action_dim; h->Sd = cfg->state_dim; h->S = h->H + 1;
   h->qd = h->nh * h->dh; h->nqkv = h->qd + 2 * h->dh; h->Bmax = cfg->max_batch; h->Lmax = cfg->max_prefix_len;
+  h->Lpmax = round_up(h->Lmax > 0 ? h->Lmax : 1, 32);
+  h->Sp = round_up(h->S, 32);
   const float* blob = static_cast<const float*>(weights_host);
-  // weights stored in bf16 mode may hold non-finite values; nothing to check
-  if (cfg->dtype == PI0X_BF16) PI0X_TRY(upload_weights<uint16_t>(h, blob));
+  if (h->bf16()) PI0X_TRY(upload_weights<uint16_t>(h, blob));
   else PI0X_TRY(upload_weights<float>(h, blob));
 
   const size_t R = (size_t)h->Bmax * h->S, AR = (size_t)h->Bmax * h->H, e = h->esz;
   PI0X_TRY(h->allocT(&h->hbuf, R * h->W * 4));
-  PI0X_TRY(h->alloc(&h->y, R * h->W * e));
-  PI0X_TRY(h->alloc(&h->qkv, R * h->nqkv * e));
+  if (h->bf16()) PI0X_TRY(h->alloc(&h->hb, R * h->W * e));
+  PI0X_TRY(h->allocT(&h->ssq, R * (h->W / 16) * 4));
+  PI0X_TRY(h->alloc(&h->qk, R * (h->qd + h->dh) * e));
+  PI0X_TRY(h->alloc(&h->vts, (size_t)h->Bmax * h->dh * h->Sp * e));
+  PI0X_HIP(hipMemset(h->vts, 0, (size_t)h->Bmax * h->dh * h->Sp * e));  // columns >= S stay zero
+  PI0X_TRY(h->alloc(&h->vtp, (size_t)h->D * h->Bmax * h->dh * h->Lpmax * e));
   PI0X_TRY(h->alloc(&h->o, R * h->qd * e));
   PI0X_TRY(h->alloc(&h->gbuf, R * h->M * e));
-  PI0X_TRY(h->alloc(&h->ain, AR * h->W * e));
   PI0X_TRY(h->alloc(&h->u, AR * h->W * e));
+  PI0X_TRY(h->allocT(&h->hs, (size_t)h->Bmax * h->W * 4));
   PI0X_TRY(h->allocT(&h->x, AR * h->A * 4));
   PI0X_TRY(h->alloc(&h->tau, (size_t)cfg->max_steps * h->W * e));
   PI0X_TRY(h->allocT(&h->tbias, (size_t)cfg->max_steps * h->W * 4));
-  PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
-  PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
-  PI0X_HIP(hipMemset(h->gemm_counters, 0, (size_t)kCounters * 4));
-  // split-KV partials for up to 512 (query tile, split) pairs; the launcher
-  // only splits when fewer than 128 query tiles exist
-  h->attn_partial_floats = (size_t)512 * (2 + h->dh / 4) * 256;
-  PI0X_TRY(h->allocT(&h->attn_partial, h->attn_partial_floats * 4));
-  PI0X_TRY(h->allocT(&h->attn_counters, (size_t)kCounters * 4));
-  PI0X_HIP(hipMemset(h->attn_counters, 0, (size_t)kCounters * 4));
+  if (!h->bf16()) {
+    PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
+    PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
+    PI0X_HIP(hipMemset(h->gemm_counters, 0, (size_t)kCounters * 4));
+  }
   PI0X_TRY(h->allocT(&h->desc, sizeof(CallDesc)));
   PI0X_HIP(hipMemset(h->desc, 0, sizeof(CallDesc)));
   const int P = h->Lmax + h->S + 1;
@@ -476,8 +702,8 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, size_t
                      h->rope_cos, h->rope_sin);
   PI0X_HIP(hipGetLastError());
   PI0X_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  if (h->bf16()) PI0X_TRY(allow_big_smem_all());
   PI0X_HIP(hipDeviceSynchronize());
-  (void)weights_bytes;
   return PI0X_OK;
 }
 
@@ -489,6 +715,8 @@ void destroy_impl(pi0x_expert* h) {
   }
   h->graphs.clear();
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+  for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
+  h->ev_pool.clear();
   for (void* p : h->allocs) (void)hipFree(p);
   h->allocs.clear();
 }
@@ -553,7 +781,7 @@ pi0x_status pi0x_expert_create(const pi0x_config* cfg, const void* weights_host,
                                     std::to_string(n * sizeof(float)));
   pi0x_expert* h = new (std::nothrow) pi0x_expert();
   if (!h) return fail(PI0X_ERR_OOM, "host allocation failed");
-  pi0x_status s = create_impl(cfg, weights_host, weights_bytes, h);
+  pi0x_status s = create_impl(cfg, weights_host, h);
   if (s != PI0X_OK) {
     std::string msg = g_err;
     destroy_impl(h);
@@ -595,5 +823,29 @@ void pi0x_expert_destroy(pi0x_expert* h) {
 }
 
 const char* pi0x_last_error(void) { return g_err.c_str(); }
+
+pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable) {
+  if (!h) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  h->timing = enable != 0;
+  return PI0X_OK;
+}
+
+pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches) {
+  if (!h || !total_ms || !launches) return fail(PI0X_ERR_INVALID_ARG, "a pointer argument is NULL");
+  for (int c = 0; c < PI0X_KERNEL_CLASSES; ++c) {
+    total_ms[c] = 0.0;
+    launches[c] = 0;
+  }
+  if (h->ev_used > 0) PI0X_HIP(hipEventSynchronize(h->ev_pool[h->ev_used - 1]));
+  for (const auto& m : h->ev_marks) {
+    float ms = 0.f;
+    PI0X_HIP(hipEventElapsedTime(&ms, h->ev_pool[m.second], h->ev_pool[m.second + 1]));
+    total_ms[m.first] += ms;
+    launches[m.first] += 1;
+  }
+  h->ev_marks.clear();
+  h->ev_used = 0;
+  return PI0X_OK;
+}
 
 }  // extern "C"

@@ -1,6 +1,5 @@
-// Bandwidth-light kernels around the GEMMs: Gemma RMSNorm, the suffix
-// embedding inputs, the sinusoidal time features, the rotary table, and the
-// final norm + action_out_proj + Euler update.
+// Bandwidth-light kernels around the GEMMs: the suffix-embedding inputs, the
+// sinusoidal time features and the rotary table.
 #pragma once
 
 #include "common.h"
@@ -18,62 +17,79 @@ __global__ void set_desc_kernel(CallDesc* d, const void* kv, const int32_t* vali
   d->t = t;
 }
 
-// Gemma RMSNorm (HF GemmaRMSNorm): y = h / sqrt(mean(h^2) + eps) * (1 + w).
-// One wave per row; scale1p holds (1 + w) in float32.
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int ldh,
-                                                      const float* __restrict__ scale1p, T* __restrict__ y,
-                                                      int ldy, int rows, int W, float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float* hr = h + (size_t)row * ldh;
-  float ss = 0.f;
-  for (int c = lane * 4; c < W; c += 256) {
-    float4 v = *reinterpret_cast<const float4*>(hr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)W + eps);
-  T* yr = y + (size_t)row * ldy;
-  for (int c = lane * 4; c < W; c += 256) {
-    float4 v = *reinterpret_cast<const float4*>(hr + c);
-    float4 s = *reinterpret_cast<const float4*>(scale1p + c);
-    yr[c + 0] = from_f32<T>(v.x * inv * s.x);
-    yr[c + 1] = from_f32<T>(v.y * inv * s.y);
-    yr[c + 2] = from_f32<T>(v.z * inv * s.z);
-    yr[c + 3] = from_f32<T>(v.w * inv * s.w);
+// State token of every sample (page 1, embed_suffix: state_proj(state)),
+// once per call: hs[b][o] = W_s s_b + b_s (float32).  The token depends on
+// neither x nor t.  One block per sample.
+__global__ __launch_bounds__(256) void state_token_kernel(const CallDesc* __restrict__ desc, int Sd, int W,
+                                                          const float* __restrict__ w_s, const float* __restrict__ b_s,
+                                                          float* __restrict__ hs) {
+  __shared__ float xs[64];
+  const int b = blockIdx.x;
+  if (threadIdx.x < Sd) xs[threadIdx.x] = desc->state[(size_t)b * Sd + threadIdx.x];
+  __syncthreads();
+  for (int o = threadIdx.x; o < W; o += 256) {
+    const float* wr = w_s + (size_t)o * Sd;
+    float s = b_s[o];
+    for (int k = 0; k < Sd; ++k) s += wr[k] * xs[k];
+    hs[(size_t)b * W + o] = s;
   }
 }
 
-// Suffix-embedding inputs (page 1, embed_suffix).  Rows r < B*H: the action
-// projection a = W_in x + b_in of action token r % H of sample r / H, written
-// to ain (model dtype) as the first operand of action_time_mlp_in.  Rows
-// r >= B*H: the state token W_s s + b_s of sample r - B*H, written to hidden
-// row (r - B*H) * S (float32).  x comes from desc->x_in when from_input, else
-// from the loop's own x buffer.  One 256-thread block per row.
+// Suffix-embedding input of one Euler step (page 1, embed_suffix).
+// Blocks < nA: 16 action rows each.  action_in_proj is folded into the action
+// half of action_time_mlp_in at create time (w_comb = W_mi,a W_in, and
+// W_mi,a b_in is part of the step bias cb), so the first layer of the time MLP
+// is u = SiLU(w_comb x + cb) with K = action_dim; u goes to the model dtype.
+// Blocks >= nA: copy the state token of one sample into hidden row b*S
+// (float32, its bf16 copy in bf16 mode, and its sum-of-squares partials over
+// groups of G columns).  x comes from desc->x_in when from_input, else from
+// the loop's own x buffer.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_inputs_kernel(const CallDesc* __restrict__ desc, const float* x_loop,
-                                                           int from_input, int B, int H, int A, int Sd, int W, int S,
-                                                           const float* __restrict__ w_in, const float* __restrict__ b_in,
-                                                           const float* __restrict__ w_s, const float* __restrict__ b_s,
-                                                           T* __restrict__ ain, float* __restrict__ hbuf, int ldh) {
-  __shared__ float xs[64];
-  const int r = blockIdx.x;
-  const bool is_state = r >= B * H;
-  const int K = is_state ? Sd : A;
-  const float* src = is_state ? desc->state + (size_t)(r - B * H) * Sd
-                              : (from_input ? desc->x_in : x_loop) + (size_t)r * A;
-  if (threadIdx.x < K) xs[threadIdx.x] = src[threadIdx.x];
-  __syncthreads();
-  const float* Wm = is_state ? w_s : w_in;
-  const float* bv = is_state ? b_s : b_in;
-  for (int o = threadIdx.x; o < W; o += 256) {
-    const float* wr = Wm + (size_t)o * K;
-    float s = 0.f;
-    for (int k = 0; k < K; ++k) s += wr[k] * xs[k];
-    s += bv[o];
-    if (is_state) hbuf[(size_t)(r - B * H) * S * ldh + o] = s;
-    else ain[(size_t)r * W + o] = from_f32<T>(s);
+__global__ __launch_bounds__(256) void suffix_in_kernel(const CallDesc* __restrict__ desc, const float* x_loop,
+                                                        int from_input, int AR, int nA, int A, int W, int S,
+                                                        const float* __restrict__ w_comb, const float* __restrict__ cb,
+                                                        T* __restrict__ u, const float* __restrict__ hs,
+                                                        float* __restrict__ hbuf, T* __restrict__ hb,
+                                                        float* __restrict__ ssq, int G) {
+  constexpr int RB = 16;
+  __shared__ float xs[RB][64];
+  if ((int)blockIdx.x < nA) {
+    const int r0 = blockIdx.x * RB;
+    const float* xsrc = from_input ? desc->x_in : x_loop;
+    for (int i = threadIdx.x; i < RB * 64; i += 256) {
+      const int rr = i / 64, a = i - rr * 64;
+      xs[rr][a] = (r0 + rr < AR && a < A) ? xsrc[(size_t)(r0 + rr) * A + a] : 0.f;
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < W; o += 256) {
+      float wr[64];
+#pragma unroll
+      for (int a = 0; a < 64; ++a) wr[a] = a < A ? w_comb[(size_t)o * A + a] : 0.f;
+      const float bias = cb[o];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        float acc = bias;
+#pragma unroll
+        for (int a = 0; a < 64; ++a) acc += wr[a] * xs[rr][a];
+        if (r0 + rr < AR) u[(size_t)(r0 + rr) * W + o] = from_f32<T>(silu(acc));
+      }
+    }
+    return;
+  }
+  const int b = blockIdx.x - nA;
+  const size_t hrow = (size_t)b * S;
+  const int np = W / G, tpg = G / 4;  // threads per column group
+  for (int c0 = threadIdx.x * 4; c0 < W; c0 += 1024) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = hs[(size_t)b * W + c0 + e];
+      hbuf[hrow * W + c0 + e] = v;
+      if (hb) hb[hrow * W + c0 + e] = from_f32<T>(v);
+      ss += v * v;
+    }
+    for (int off = 1; off < tpg; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x % tpg) == 0) ssq[hrow * np + c0 / G] = ss;
   }
 }
 
@@ -109,64 +125,6 @@ __global__ void rope_table_kernel(int P, int d, double base, float* __restrict__
   const double theta = (double)p * pow(base, -2.0 * (double)j / (double)d);
   cos_t[i] = (float)cos(theta);
   sin_t[i] = (float)sin(theta);
-}
-
-// Final norm on the action rows, action_out_proj and the Euler step
-// (page 1, denoise_step's last lines and sample_actions' update).  One wave
-// per action row r = b*H + i (hidden row b*S + 1 + i).  mode 0: x <- x + dt v
-// (x read from desc->x_in when from_input, else x_loop; written to x_loop, and
-// also to desc->out when write_out); mode 1: v written to desc->out.
-// W_out float32 [A][W]; A <= 64; W a multiple of 256.
-__global__ __launch_bounds__(256) void final_kernel(const CallDesc* __restrict__ desc, const float* __restrict__ h,
-                                                    int ldh, const float* __restrict__ scale1p,
-                                                    const float* __restrict__ w_out, const float* __restrict__ b_out,
-                                                    float* x_loop, int from_input, int write_out, int mode, float dt,
-                                                    int rows, int H, int S, int W, int A, float eps) {
-  __shared__ float red[4][64][65];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
-  const bool ok = r < rows;
-  float part[64];
-#pragma unroll
-  for (int o = 0; o < 64; ++o) part[o] = 0.f;
-  if (ok) {
-    const int hrow = (r / H) * S + 1 + r % H;
-    const float* hr = h + (size_t)hrow * ldh;
-    float ss = 0.f;
-    for (int c = lane * 4; c < W; c += 256) {
-      float4 v = *reinterpret_cast<const float4*>(hr + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)W + eps);
-    for (int c = lane * 4; c < W; c += 256) {
-      float4 v = *reinterpret_cast<const float4*>(hr + c);
-      float4 s = *reinterpret_cast<const float4*>(scale1p + c);
-      const float y0 = v.x * inv * s.x, y1 = v.y * inv * s.y, y2 = v.z * inv * s.z, y3 = v.w * inv * s.w;
-#pragma unroll
-      for (int o = 0; o < 64; ++o) {
-        if (o < A) {
-          float4 wv = *reinterpret_cast<const float4*>(w_out + (size_t)o * W + c);
-          part[o] += wv.x * y0 + wv.y * y1 + wv.z * y2 + wv.w * y3;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 0; o < 64; ++o) red[wave][lane][o] = part[o];
-  __syncthreads();
-  if (!ok || lane >= A) return;
-  float v = b_out[lane];
-  for (int l = 0; l < 64; ++l) v += red[wave][l][lane];
-  const size_t idx = (size_t)r * A + lane;
-  if (mode == 1) {
-    desc->out[idx] = v;
-  } else {
-    const float x = (from_input ? desc->x_in : x_loop)[idx];
-    const float xn = x + dt * v;
-    x_loop[idx] = xn;
-    if (write_out) desc->out[idx] = xn;
-  }
 }
 
 }  // namespace pi0x
