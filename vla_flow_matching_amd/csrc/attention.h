@@ -6,20 +6,21 @@
 // shared by all query heads, so the num_heads * S queries of a sample (query
 // index qi = s*num_heads + n) form one matrix against one key/value sequence.
 //
-// Keys are visited in blocks of 32.  A wave computes S^T = K Q^T with the
-// matrix cores, so a lane holds 8 scores of its own query (lane % 16); the
-// online softmax runs in float32 in registers, and O^T = V^T P^T reuses those
-// 8 probabilities directly as the MFMA operand.  V is read transposed
-// ([head_dim][keys]): the prefix values are transposed once per call by
-// transpose_v_kernel, the suffix values are written transposed by the q/k/v
-// projection.  Masked keys get probability exactly 0; padded prefix keys are
-// never read from the caller's cache (zeros are used instead).
+// attn_kernel: a block of 8 waves owns 128 queries (16 per wave).  Keys are
+// staged in blocks of KB (64 for bf16, 32 for fp32): K row-major and V
+// transposed ([head_dim][keys]) are copied into LDS with 16-byte accesses and
+// shared by the 8 waves, double-buffered so the global loads of block i+1
+// overlap the matrix-core work on block i.  A wave computes S^T = K Q^T, so a
+// lane holds the scores of its own query (lane % 16); the online softmax runs
+// in float32 in registers and O^T = V^T P^T reuses those probabilities
+// directly as the MFMA operand.  The prefix values are transposed once per
+// call by transpose_v_kernel, the suffix values are written transposed by the
+// q/k/v projection.  Masked keys get probability exactly 0; padded prefix keys
+// are never read from the caller's cache (zeros are used instead).
 //
-// attn_kernel: 4 waves x 16 queries share each staged K / V^T block in LDS
-// (large batches).  attn_small_kernel: 8 waves split the key blocks of the
-// same 16 queries, load operands straight from L2, and merge their partial
-// softmax states through LDS at the end (batch 1, where 64-query tiles would
-// leave most of the chip idle).
+// With splits > 1 (small batches) the key blocks of a sample are divided over
+// gridDim.z; each split writes its running max, sum and unnormalised output
+// and attn_combine_kernel merges them in split order.
 #pragma once
 
 #include "common.h"
@@ -39,88 +40,101 @@ struct AttnArgs {
   void* out;  // [B*S][ldo], head n of token s at column n*head_dim
   int ldo;
   float scale;
+  int splits;
+  float* partial;  // splits > 1: [B][tiles][splits][2 + head_dim/4][512]
 };
+
+template <typename T> struct AttnCfg;
+template <> struct AttnCfg<bf16> { static constexpr int KB = 64; };
+template <> struct AttnCfg<float> { static constexpr int KB = 32; };
+
+template <typename T, int DH>
+constexpr size_t attn_smem_bytes() {
+  constexpr int KB = AttnCfg<T>::KB, VE = 16 / (int)sizeof(T);
+  return (size_t)2 * (KB * (DH + VE) + DH * (KB + VE)) * sizeof(T);
+}
 
 // exp for the softmax: the hardware exp2 path in bf16 mode, libm expf in float32 mode.
 template <typename T> __device__ __forceinline__ float fexp(float x) { return expf(x); }
 template <> __device__ __forceinline__ float fexp<bf16>(float x) { return __expf(x); }
 
-// Per-wave online-softmax state for 16 queries (lane % 16) and head_dim DH.
 template <typename T, int DH>
-struct SoftmaxState {
-  static constexpr int ND = DH / 16;
-  f32x4 o[ND];
-  float m = -INFINITY, l = 0.f;  // running max (same on the 4 lanes of a query), this lane's share of the sum
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // st[kt][e]: score of this lane's query vs key kt*16 + 4g + e of the block (already masked to -inf).
-  // Returns the probabilities as the PV operand (key order (e/4)*16 + 4g + e%4).
-  __device__ __forceinline__ Frag<T> update(const float (&s)[8]) {
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bmax = fmaxf(bmax, s[i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m, bmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fexp<T>(m - m_new);
-    Frag<T> pf;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e = (s[i] == -INFINITY) ? 0.f : fexp<T>(s[i] - m_new);
-      l += e;
-      set_frag(pf, i, e);
-    }
-    m = m_new;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      o[d][0] *= alpha; o[d][1] *= alpha; o[d][2] *= alpha; o[d][3] *= alpha;
-    }
-    return pf;
-  }
-};
-
-// Scores of one 32-key block, masked: keys >= lim do not exist; in the suffix
-// (pre == false) the state query (qs == 0) only sees key 0.
-__device__ __forceinline__ void mask_scores(const f32x4 (&st)[2], float scale, int base, int lim, bool pre, int qs,
-                                            int g, float (&s)[8]) {
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = base + kt * 16 + g * 4 + e;
-      bool vis = key < lim;
-      if (!pre) vis = vis && (qs >= 1 || key == 0);
-      s[kt * 4 + e] = vis ? st[kt][e] * scale : -INFINITY;
-    }
-}
-
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int KB = 32;
+__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+  constexpr int KB = AttnCfg<T>::KB;
+  constexpr int KT = KB / 16;   // 16-key score tiles per block
+  constexpr int KS = KB / 32;   // 32-key PV steps per block
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int LDK = DH + VE;  // padded K row
   constexpr int LDV = KB + VE;  // padded V^T row
   constexpr int NC = DH / 32, ND = DH / 16;
-  __shared__ __attribute__((aligned(16))) T Ks[KB * LDK];
-  __shared__ __attribute__((aligned(16))) T Vt[DH * LDV];
+  constexpr int NVEC = KB * DH / VE;        // 16-byte vectors of K (and of V^T) per key block
+  constexpr int KVEC = (NVEC + 511) / 512;  // per thread
+  constexpr bool FULL = NVEC % 512 == 0;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  T* Ks = reinterpret_cast<T*>(smem_raw);  // [2][KB * LDK]
+  T* Vt = Ks + 2 * KB * LDK;               // [2][DH * LDV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x, b = blockIdx.y;
+  const int tile = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int nq = a.nh * a.S;
-  const int qi = tile * 64 + wave * 16 + (lane & 15);
+  const int qi = tile * 128 + wave * 16 + (lane & 15);
   const bool qok = qi < nq;
   const int qs = qok ? qi / a.nh : 0, qn = qok ? qi - qs * a.nh : 0;
 
-  int valid = a.desc->valid[b];
+  // uniform over the block: keeps the key-block loop in scalar registers
+  int valid = __builtin_amdgcn_readfirstlane(a.desc->valid[b]);
   valid = valid < 0 ? 0 : (valid > a.L ? a.L : valid);
   const T* __restrict__ qk = reinterpret_cast<const T*>(a.qk);
   const T* Kp = reinterpret_cast<const T*>(a.desc->kv) + a.kv_k_off + (size_t)b * a.L * DH;
   const T* Vtp = reinterpret_cast<const T*>(a.vtp) + (size_t)b * DH * a.Lp;
   const T* Vts = reinterpret_cast<const T*>(a.vts) + (size_t)b * DH * a.Sp;
   const T* Sq = qk + (size_t)b * a.S * a.ldqk;
+
+  const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
+  const int nblk = nb_pre + nb_suf;
+  const int blk_b = (int)((long)split * nblk / a.splits), blk_e = (int)((long)(split + 1) * nblk / a.splits);
+
+  // staging of key block blk into registers; keys past the limit become
+  // zeros when stored to LDS (masking at load time would wait on the load)
+  u32x4 rk[KVEC], rv[KVEC];
+  unsigned kzero = 0;
+  auto gload = [&](int blk) {
+    const bool pre = blk < nb_pre;
+    const int base = pre ? blk * KB : (blk - nb_pre) * KB;
+    const int lim = pre ? valid : a.S;
+    kzero = 0;
+#pragma unroll
+    for (int i = 0; i < KVEC; ++i) {
+      const int v = tid + i * 512, kk = v / (DH / VE), dc = v % (DH / VE), key = base + kk;
+      if (!FULL && v >= NVEC) break;
+      const T* src = pre ? Kp + (size_t)min(key, max(lim - 1, 0)) * DH : Sq + (size_t)min(key, lim - 1) * a.ldqk + a.col_k;
+      rk[i] = gload16(src + dc * VE);
+      kzero |= (key >= lim ? 1u : 0u) << i;
+    }
+#pragma unroll
+    for (int i = 0; i < KVEC; ++i) {
+      const int v = tid + i * 512, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
+      if (!FULL && v >= NVEC) break;
+      const T* src = pre ? Vtp + (size_t)d * a.Lp + base + kc : Vts + (size_t)d * a.Sp + base + kc;
+      rv[i] = gload16(src);
+    }
+  };
+  auto sstore = [&](int st) {
+    T* ks = Ks + st * KB * LDK;
+    T* vt = Vt + st * DH * LDV;
+#pragma unroll
+    for (int i = 0; i < KVEC; ++i) {
+      const int v = tid + i * 512, kk = v / (DH / VE), dc = v % (DH / VE);
+      if (!FULL && v >= NVEC) break;
+      *reinterpret_cast<u32x4*>(&ks[kk * LDK + dc * VE]) = ((kzero >> i) & 1u) ? u32x4{0u, 0u, 0u, 0u} : rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < KVEC; ++i) {
+      const int v = tid + i * 512, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
+      if (!FULL && v >= NVEC) break;
+      *reinterpret_cast<u32x4*>(&vt[d * LDV + kc]) = rv[i];
+    }
+  };
 
   Frag<T> qf[NC];
   {
@@ -133,184 +147,150 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int i = 0; i < 8; ++i) set_frag(qf[c], i, 0.f);
     }
   }
-  const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
-  SoftmaxState<T, DH> sm;
-  sm.init();
+  f32x4 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // running max (same on the 4 lanes of a query), this lane's share of the sum
 
-  for (int blk = 0; blk < nb_pre + nb_suf; ++blk) {
+  // unconditional (an empty split stages a block it never reads) so that
+  // every path into the loop has waited for all loads issued so far
+  gload(min(blk_b, nblk - 1));
+  sstore(0);
+  int st = 0;
+  for (int blk = blk_b; blk < blk_e; ++blk) {
+    const bool more = blk + 1 < blk_e;
+    if (more) gload(blk + 1);
+    __syncthreads();
+    const T* ks = Ks + st * KB * LDK;
+    const T* vt = Vt + st * DH * LDV;
     const bool pre = blk < nb_pre;
     const int base = pre ? blk * KB : (blk - nb_pre) * KB;
     const int lim = pre ? valid : a.S;
-    constexpr int KVPR = DH / VE;  // 16-byte vectors per K row
-#pragma unroll
-    for (int it = 0; it < (KB * KVPR + 255) / 256; ++it) {
-      const int v = tid + it * 256;
-      if (v < KB * KVPR) {
-        const int kk = v / KVPR, dc = v - kk * KVPR, key = base + kk;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (key < lim) {
-          const T* src = pre ? Kp + (size_t)key * DH : Sq + (size_t)key * a.ldqk + a.col_k;
-          val = *reinterpret_cast<const uint4*>(src + dc * VE);
-        }
-        *reinterpret_cast<uint4*>(&Ks[kk * LDK + dc * VE]) = val;
-      }
-    }
-    constexpr int VPR = KB / VE;  // 16-byte vectors per V^T row of the block
-#pragma unroll
-    for (int it = 0; it < (DH * VPR + 255) / 256; ++it) {
-      const int v = tid + it * 256;
-      if (v < DH * VPR) {
-        const int d = v / VPR, kc = (v - d * VPR) * VE;
-        const T* src = pre ? Vtp + (size_t)d * a.Lp + base + kc : Vts + (size_t)d * a.Sp + base + kc;
-        *reinterpret_cast<uint4*>(&Vt[d * LDV + kc]) = *reinterpret_cast<const uint4*>(src);
-      }
-    }
-    __syncthreads();
 
-    f32x4 st[2];
+    // scores: lane holds its query vs key kt*16 + 4g + e of the block
+    float s[KT][4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; ++kt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         Frag<T> kf;
-        load8(kf, &Ks[(kt * 16 + (lane & 15)) * LDK + c * 32 + g * 8]);
-        mma32(kf, qf[c], st[kt]);
+        load8(kf, &ks[(kt * 16 + (lane & 15)) * LDK + c * 32 + g * 8]);
+        mma32(kf, qf[c], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = base + kt * 16 + g * 4 + e;
+        bool vis = key < lim;
+        if (!pre) vis = vis && (qs >= 1 || key == 0);
+        s[kt][e] = vis ? acc[e] * a.scale : -INFINITY;
       }
     }
-    float s[8];
-    mask_scores(st, a.scale, base, lim, pre, qs, g, s);
-    const Frag<T> pf = sm.update(s);
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, s[kt][e]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float m_new = fmaxf(m_run, bmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fexp<T>(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      Frag<T> vf;
-      const T* vrow = &Vt[(d * 16 + (lane & 15)) * LDV];
-      load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
-      mma32(vf, pf, sm.o[d]);
+      o[d][0] *= alpha; o[d][1] *= alpha; o[d][2] *= alpha; o[d][3] *= alpha;
     }
-    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < KS; ++ks2) {
+      // probabilities of keys 32*ks2 + (i/4)*16 + 4g + i%4 as the PV operand
+      Frag<T> pf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = s[2 * ks2 + i / 4][i % 4];
+        const float e = (x == -INFINITY) ? 0.f : fexp<T>(x - m_new);
+        l_run += e;
+        set_frag(pf, i, e);
+      }
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        Frag<T> vf;
+        const T* vrow = &vt[(d * 16 + (lane & 15)) * LDV + ks2 * 32];
+        load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
+        mma32(vf, pf, o[d]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) sstore(st ^ 1);
+    st ^= 1;
   }
 
-  float l_tot = sm.l + __shfl_xor(sm.l, 16, 64);
+  // lane holds O[q][d*16 + 4g + e] (unnormalised); total softmax denominator of its query
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (a.splits > 1) {
+    constexpr int NR = 2 + ND * 4;
+    float* mine = a.partial + (((size_t)b * gridDim.x + tile) * a.splits + split) * NR * 512;
+    mine[tid] = m_run;
+    mine[512 + tid] = l_tot;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine[(2 + d * 4 + e) * 512 + tid] = o[d][e];
+    return;
+  }
   if (!qok) return;
   const float inv = 1.f / l_tot;
   T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(sm.o[d][e] * inv);
+    for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(o[d][e] * inv);
 }
 
+// Merges the split partial softmax states of attn_kernel in split order.
+// Grid (tiles, B, head_dim / 16): thread tid of the block takes the query
+// that thread tid of attn_kernel held and the 4 output features of d-tile
+// blockIdx.z it held there.
+template <int DH> constexpr int attn_combine_dc() { return 1; }
+template <int DH> constexpr int attn_combine_chunks() { return DH / 16; }
+
 template <typename T, int DH>
-__global__ __launch_bounds__(512) void attn_small_kernel(AttnArgs a) {
-  constexpr int KB = 32, NW = 8;
-  constexpr int NC = DH / 32, ND = DH / 16;
-  constexpr int NR = 2 + ND * 4;  // floats per lane in the merge buffer
-  __shared__ float red[NW * 64 * NR];
-
+__global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
+  constexpr int ND = DH / 16, NR = 2 + ND * 4, DC = attn_combine_dc<DH>(), NV = DC * 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x, b = blockIdx.y;
+  const int tile = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * DC;
   const int nq = a.nh * a.S;
-  const int qi = tile * 16 + (lane & 15);
-  const bool qok = qi < nq;
-  const int qs = qok ? qi / a.nh : 0, qn = qok ? qi - qs * a.nh : 0;
-
-  int valid = a.desc->valid[b];
-  valid = valid < 0 ? 0 : (valid > a.L ? a.L : valid);
-  const T* __restrict__ qk = reinterpret_cast<const T*>(a.qk);
-  const T* Kp = reinterpret_cast<const T*>(a.desc->kv) + a.kv_k_off + (size_t)b * a.L * DH;
-  const T* Vtp = reinterpret_cast<const T*>(a.vtp) + (size_t)b * DH * a.Lp;
-  const T* Vts = reinterpret_cast<const T*>(a.vts) + (size_t)b * DH * a.Sp;
-  const T* Sq = qk + (size_t)b * a.S * a.ldqk;
-
-  Frag<T> qf[NC];
-  {
-    const T* qrow = Sq + (size_t)qs * a.ldqk + qn * DH;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (qok) load8(qf[c], qrow + c * 32 + g * 8);
-      else
-#pragma unroll
-        for (int i = 0; i < 8; ++i) set_frag(qf[c], i, 0.f);
-    }
-  }
-  const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
-  SoftmaxState<T, DH> sm;
-  sm.init();
-
-  for (int blk = wave; blk < nb_pre + nb_suf; blk += NW) {
-    const bool pre = blk < nb_pre;
-    const int base = pre ? blk * KB : (blk - nb_pre) * KB;
-    const int lim = pre ? valid : a.S;
-    f32x4 st[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = base + kt * 16 + (lane & 15);
-      const bool kok = key < lim;
-      const T* krow = pre ? Kp + (size_t)key * DH : Sq + (size_t)key * a.ldqk + a.col_k;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        Frag<T> kf;
-        if (kok) load8(kf, krow + c * 32 + g * 8);
-        else
-#pragma unroll
-          for (int i = 0; i < 8; ++i) set_frag(kf, i, 0.f);
-        mma32(kf, qf[c], st[kt]);
-      }
-    }
-    float s[8];
-    mask_scores(st, a.scale, base, lim, pre, qs, g, s);
-    const Frag<T> pf = sm.update(s);
-    const T* vbase = pre ? Vtp + base : Vts + base;
-    const int vld = pre ? a.Lp : a.Sp;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      Frag<T> vf;
-      const T* vrow = vbase + (size_t)(d * 16 + (lane & 15)) * vld;
-      load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
-      mma32(vf, pf, sm.o[d]);
-    }
-  }
-
-  // merge the 8 waves' states: lane layout (q = lane % 16, g = lane / 16), O^T element d*16 + 4g + e
-  float* mine = red + (wave * 64 + lane) * NR;
-  mine[0] = sm.m;
-  mine[1] = sm.l;
-#pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mine[2 + d * 4 + e] = sm.o[d][e];
-  __syncthreads();
-  const int ln = tid & 63, q = ln & 15;
-  const int qi2 = tile * 16 + q;
-  if (qi2 >= nq) return;
-  const int qs2 = qi2 / a.nh, qn2 = qi2 - qs2 * a.nh;
+  const int qi = tile * 128 + wave * 16 + (lane & 15);
+  if (qi >= nq) return;
+  const int qs = qi / a.nh, qn = qi - qs * a.nh;
+  const float* P = a.partial + ((size_t)b * gridDim.x + tile) * a.splits * NR * 512 + tid;
   float mz = -INFINITY;
+#pragma unroll 8
+  for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * NR * 512]);
+  float l = 0.f;
+  float o[NV];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) mz = fmaxf(mz, red[(w * 64 + ln) * NR]);
-  float wt[NW], lsum = 0.f;
+  for (int i = 0; i < NV; ++i) o[i] = 0.f;
+#pragma unroll 2
+  for (int z = 0; z < a.splits; ++z) {
+    const float* pz = P + (size_t)z * NR * 512;
+    float v[2 + NV];
+    v[0] = pz[0];
+    v[1] = pz[512];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float mw = red[(w * 64 + ln) * NR];
-    wt[w] = (mw == -INFINITY) ? 0.f : fexp<T>(mw - mz);
-    float lw = 0.f;
+    for (int i = 0; i < NV; ++i) v[2 + i] = pz[(2 + d0 * 4 + i) * 512];
+    const float w = (v[0] == -INFINITY) ? 0.f : fexp<T>(v[0] - mz);
+    l += w * v[1];
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) lw += red[(w * 64 + gg * 16 + q) * NR + 1];
-    lsum += wt[w] * lw;
+    for (int i = 0; i < NV; ++i) o[i] += w * v[2 + i];
   }
-  const float inv = 1.f / lsum;
-  T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs2) * a.ldo + qn2 * DH;
-  const int g2 = ln >> 4;
-  for (int d = tid >> 6; d < ND; d += NW)
+  const float inv = 1.f / l;
+  T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float acc = 0.f;
+  for (int d = 0; d < DC; ++d)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc += wt[w] * red[(w * 64 + ln) * NR + 2 + d * 4 + e];
-      orow[d * 16 + g2 * 4 + e] = from_f32<T>(acc * inv);
-    }
+    for (int e = 0; e < 4; ++e) orow[(d0 + d) * 16 + g * 4 + e] = from_f32<T>(o[d * 4 + e] * inv);
 }
 
 // Prefix values, transposed once per call: vt[l][b][d][Lp] = V_l[b][key][d] for

@@ -24,18 +24,17 @@ struct CallDesc {
   float t;               // single step: the time value
 };
 
-// float -> bfloat16, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  uint16_t r;
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) {
-    r = (uint16_t)((u >> 16) | 0x40u);
-  } else {
-    u += 0x7fffu + ((u >> 16) & 1u);
-    r = (uint16_t)(u >> 16);
-  }
-  return __builtin_bit_cast(bf16, r);
+// 16-byte load through a global-address-space pointer.  Pointers read from
+// memory (the call descriptor) are generic to the compiler; generic loads
+// also count against the LDS counter, so a later LDS wait would stall on them.
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
+      (const __attribute__((address_space(1))) void*)p);
 }
+
+// float -> bfloat16, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }

@@ -11,12 +11,12 @@
 //                     block tiles with 2x2 waves of 64x64 / 128x128 and K
 //                     slices of 64 double-buffered through padded LDS: the
 //                     compute-bound shapes (batch >= 2).
-//  * gemm_skinny_kernel  bf16, M <= 64: the weight-streaming shapes (batch 1).
-//                     No LDS staging of operands: each of 8 waves streams an
-//                     eighth of the K range with 32-byte loads per lane, the
-//                     next 64-wide K slice in flight while the current one
-//                     feeds the MFMAs, and the waves' tiles are summed through
-//                     LDS.
+//  * gemm_wide_kernel  bf16, M <= 64, wide N (batch 1): one block per 16-32
+//                     columns over the whole K range, all loads in flight at
+//                     once, epilogue in the same kernel.
+//  * gemm_stream_kernel + gemm_reduce_kernel  bf16, M <= 64, narrow N or long
+//                     K (batch 1): split over N and K, the K-split partials
+//                     summed by the epilogue kernel.
 //
 // RMSNorm fusion.  The Gemma norm in front of the q/k/v and gate/up
 // projections is y = h / rms(h) * (1 + w); (1 + w) is folded into the weight
@@ -138,9 +138,10 @@ struct EpiResidual {
 
 // Fused q/k/v projection epilogue (after the inv_rms row scale): rotate-half
 // RoPE on every q head and the k head at position valid_len[b] + s for suffix
-// token s of sample b (float32 cos/sin table [position][head_dim/2]).  q and k
-// go to out[row][q heads | k] in the natural layout; the values go transposed
-// to vt[b][d][vt_ld] (column s), the layout attention reads them in.
+// token s of sample b; the (cos, sin) pairs of every suffix row are tabulated
+// once per call in cs[row][head_dim/2].  q and k go to out[row][q heads | k] in
+// the natural layout; the values go transposed to vt[b][d][vt_ld] (column s),
+// the layout attention reads them in.
 template <typename T>
 struct EpiQkvRope {
   static constexpr bool kPaired = true, kRowScale = true, kSsq = false;
@@ -148,10 +149,8 @@ struct EpiQkvRope {
   T* out;
   int ldo;
   int qk_cols;  // (num_heads + 1) * head_dim
-  int head_dim, S, L;
-  const CallDesc* desc;
-  const float* cos_t;
-  const float* sin_t;
+  int head_dim, S;
+  const float2* cs;
   T* vt;
   int vt_ld;
   __device__ __forceinline__ int jj(int c) const {
@@ -160,18 +159,14 @@ struct EpiQkvRope {
   }
   __device__ __forceinline__ Pre fetch(int row, int c) const {
     if (c >= qk_cols) return float2{0.f, 0.f};
-    const int b = row / S, s = row - b * S;
-    int v = desc->valid[b];
-    v = v < 0 ? 0 : (v > L ? L : v);
-    const size_t t = (size_t)(v + s) * (head_dim >> 1) + jj(c);
-    return float2{cos_t[t], sin_t[t]};
+    return cs[(size_t)row * (head_dim >> 1) + jj(c)];
   }
-  __device__ __forceinline__ void pair(int row, int c, float x1, float x2, Pre cs) const {
+  __device__ __forceinline__ void pair(int row, int c, float x1, float x2, Pre cs_) const {
     if (c < qk_cols) {
       const int half = head_dim >> 1;
       T* o = out + (size_t)row * ldo + (c / head_dim) * head_dim + jj(c);
-      o[0] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-      o[half] = from_f32<T>(x2 * cs.x + x1 * cs.y);
+      o[0] = from_f32<T>(x1 * cs_.x - x2 * cs_.y);
+      o[half] = from_f32<T>(x2 * cs_.x + x1 * cs_.y);
     } else {
       const int b = row / S, s = row - b * S;
       T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + s;
@@ -597,86 +592,75 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, Epi epi) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm_skinny_kernel: bf16, M <= 64 rows, BN (16/32/64) output columns per block
+// gemm_wide_kernel: bf16, M <= 64 rows, BN = 16*TN output columns per block
+// and the whole K range, split evenly over NW waves (K / NW <= 256 elements
+// each).  Every wave issues all of its loads at once -- its weight rows and
+// its slice of all 64 activation rows (rows past M repeat row M-1) -- so one
+// memory round trip covers the block; the waves' tiles are then summed
+// through LDS and the epilogue runs in the same kernel.  Used where N alone
+// gives enough blocks to cover the chip.
 // ---------------------------------------------------------------------------
-template <int BN, class Epi>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs g, Epi epi) {
-  constexpr int NW = 8;                         // waves; each takes 1/8 of the K range
-  constexpr int TN = BN / 16, TM = 4, KS = 64;  // K super-slice: two 16x16x32 MFMA steps
-  constexpr int LDR = BN + 1;
-  constexpr int TPR = 512 / 64;                 // epilogue threads per row
-  constexpr int CPT = BN / TPR;                 // columns per thread in the epilogue
-  static_assert(!Epi::kPaired || BN >= 32, "paired epilogues need 32-column groups");
+template <int NW, int TN, class Epi>
+__global__ __launch_bounds__(NW * 64) void gemm_wide_kernel(GemmArgs g, Epi epi) {
+  constexpr int NT = NW * 64, BN = TN * 16, LDR = BN + 1;
+  constexpr int TPR = NT / 64;      // epilogue threads per row
+  constexpr int CPT = BN / TPR;     // columns per thread in the epilogue
+  constexpr int KW = 256, NP = KW / 64;  // largest K share of a wave, in 64-wide chunks
+  static_assert(!Epi::kPaired || (BN >= 32 && CPT % 2 == 0), "paired epilogues need 32-column groups");
+  static_assert(CPT >= 1, "too many threads for the tile");
   __shared__ float red[NW][64 * LDR];
   __shared__ float s_inv[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN;
-  const int KI = g.K / KS;
-  const int wb = KI * wave / NW, we = KI * (wave + 1) / NW;
+  const int kw = g.K / NW, kb = wave * kw;  // this wave's K range [kb, kb + kw), kw % 64 == 0, kw <= KW
   const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
 
   if constexpr (Epi::kRowScale) row_scale_prologue(g, 0, 64, s_inv);
 
-  // lane (l%16, l/16): row/column l%16 of each 16-tile, K elements 16*(l/16) .. +15 of a super-slice
+  // lane (r, q) = (l % 16, l / 16): row/column r of each 16-tile, elements 16q .. 16q+15 of each
+  // 64-wide chunk (two MFMA steps of 8)
   const int fr = lane & 15, fk = (lane >> 4) * 16;
-  const bf16* wp = W + (size_t)(n0 + fr) * g.ldw + fk;
-  // rows past M read row M-1 (unconditional loads); their results are never stored
-  const bf16* ap[TM];
+  u32x4 wv[TN][NP][2], av[4][NP][2];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) ap[i] = A + (size_t)min(i * 16 + fr, g.M - 1) * g.lda + fk;
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // two register stages: the loads of slice k+1 are in flight while slice k feeds the MFMAs
-  u32x4 wv[2][TN][2], av[2][TM][2];
-  auto load = [&](int st, int k) {
-    const size_t ko = (size_t)k * KS;
+  for (int p = 0; p < NP; ++p) {
+    if (p * 64 >= kw) break;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(wp + (size_t)j * 16 * g.ldw + ko);
-      wv[st][j][0] = p[0];
-      wv[st][j][1] = p[1];
+      const bf16* src = W + (size_t)(n0 + j * 16 + fr) * g.ldw + kb + p * 64 + fk;
+      wv[j][p][0] = gload16(src);
+      wv[j][p][1] = gload16(src + 8);
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(ap[i] + ko);
-      av[st][i][0] = p[0];
-      av[st][i][1] = p[1];
+    for (int i = 0; i < 4; ++i) {
+      const bf16* src = A + (size_t)min(i * 16 + fr, g.M - 1) * g.lda + kb + p * 64 + fk;
+      av[i][p][0] = gload16(src);
+      av[i][p][1] = gload16(src + 8);
     }
-  };
-  auto compute = [&](int st) {
+  }
+  f32x4 acc[4][TN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (p * 64 >= kw) break;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[st][i][hh]),
-                                                              __builtin_bit_cast(bf16x8, wv[st][j][hh]), acc[i][j],
-                                                              0, 0, 0);
-  };
-  if (wb < we) load(0, wb);
-  for (int k = wb; k < we; k += 2) {
-    if (k + 1 < we) load(1, k + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    if (k + 1 < we) {
-      if (k + 2 < we) load(0, k + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i][p][hh]),
+                                                              __builtin_bit_cast(bf16x8, wv[j][p][hh]), acc[i][j], 0, 0, 0);
   }
 
   // sum the waves' tiles
   float* r = red[wave];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -706,19 +690,144 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs g, Epi epi) {
       if (ok) epi.pair(row, n0 + c, tot(c), tot(c + 16), pre[e]);
     }
   } else {
+    static_assert(!Epi::kSsq, "residual producers use the stream kernels (256-column sum-of-squares groups)");
     typename Epi::Pre pre[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) pre[e] = epi.fetch(frow, n0 + q * CPT + e);
-    float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
       const int c = q * CPT + e;
-      if (ok) ss += epi.one(row, n0 + c, tot(c), pre[e]);
+      if (ok) epi.one(row, n0 + c, tot(c), pre[e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_stream_kernel + gemm_reduce_kernel: bf16, M <= 64 rows (batch 1).
+// The weights are the only large operand, so the work is split over both N
+// (64 columns per block, 16 per wave) and K (KB per block) to put every CU on
+// the weight stream: a block issues all its weight loads (KB/4 elements per
+// lane) and its share of the activation slice [64][KB] at once, stages the
+// activations in LDS for its 4 waves and writes a float32 partial tile
+// [M][64] to partial[k-split].  gemm_reduce_kernel then adds the K-split
+// partials in split order and runs the epilogue, one wave per (row, 256
+// columns) -- 512 for paired epilogues.  Residual producers (kSsq) therefore
+// write one sum-of-squares partial per 256 columns.
+// ---------------------------------------------------------------------------
+constexpr int kStreamGroup = 256;  // columns per reduce wave (non-paired)
+
+template <int KB>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+  constexpr int LDA = KB + 8;          // padded LDS row (bf16 elements)
+  constexpr int NP = KB / 64;          // 64-wide K chunks
+  constexpr int AV = 64 * KB / 8 / 256;  // 16-byte activation vectors per thread
+  __shared__ __attribute__((aligned(16))) bf16 As[64 * LDA];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 64 + wave * 16, k0 = blockIdx.y * KB;
+  const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
+  const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
+
+  // lane (r, q) = (l % 16, l / 16): weight row n0 + r, elements 16q .. 16q+15 of every 64-wide chunk
+  // (the first 8 feed one MFMA step, the next 8 another; the activations use the same K order)
+  const bf16* wp = W + (size_t)(n0 + (lane & 15)) * g.ldw + k0 + (lane >> 4) * 16;
+  u32x4 wv[NP][2];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    wv[p][0] = gload16(wp + p * 64);
+    wv[p][1] = gload16(wp + p * 64 + 8);
+  }
+  // activation rows past M repeat row M-1; their results are never stored
+  u32x4 av[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int v = tid + i * 256, r = v / (KB / 8), c = (v % (KB / 8)) * 8;
+    av[i] = gload16(A + (size_t)min(r, g.M - 1) * g.lda + k0 + c);
+  }
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int v = tid + i * 256, r = v / (KB / 8), c = (v % (KB / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&As[r * LDA + c]) = av[i];
+  }
+  __syncthreads();
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[(i * 16 + (lane & 15)) * LDA + p * 64 + (lane >> 4) * 16 + hh * 8]);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wv[p][hh]), acc[i], 0, 0, 0);
+      }
+
+  float* P = g.partial + (size_t)blockIdx.y * g.M * g.N + n0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = i * 16 + (lane >> 4) * 4 + e;
+      if (row < g.M) P[(size_t)row * g.N] = acc[i][e];
+    }
+}
+
+// Sum of the g.splits K-split partials of 4 consecutive columns of a row, in
+// split order.  Loads go out 16 at a time (indices past the last split re-read
+// it and are dropped), so a reduce costs one memory round trip per 16 splits.
+__device__ __forceinline__ f32x4 sum_splits(const GemmArgs& g, int row, int c0) {
+  const size_t plane = (size_t)g.M * g.N;
+  const float* p = g.partial + (size_t)row * g.N + c0;
+  f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < g.splits; k0 += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = *reinterpret_cast<const f32x4*>(p + (size_t)min(k0 + k, g.splits - 1) * plane);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < g.splits) t += v[k];
+  }
+  return t;
+}
+
+template <class Epi>
+__global__ __launch_bounds__(64) void gemm_reduce_kernel(GemmArgs g, Epi epi) {
+  const int lane = threadIdx.x, row = blockIdx.y;
+  float sc = 1.f;
+  if constexpr (Epi::kRowScale) {
+    float s = 0.f;
+    const float* p = g.ssq_in + (size_t)row * g.ssq_np;
+    for (int i = 0; i < g.ssq_np; ++i) s += p[i];
+    sc = 1.0f / sqrtf(s / (float)g.norm_dim + g.norm_eps);
+  }
+  if constexpr (Epi::kPaired) {
+    // lane: columns c0 .. c0+3 (c0 % 32 < 16) and their partners c0+16 .. c0+19
+    const int q = blockIdx.x * 64 + lane;
+    const int c0 = (q >> 2) * 32 + (q & 3) * 4;
+    if (c0 >= g.N) return;
+    typename Epi::Pre pre[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pre[e] = epi.fetch(row, c0 + e);
+    const f32x4 lo = sum_splits(g, row, c0), hi = sum_splits(g, row, c0 + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) epi.pair(row, c0 + e, sc * lo[e], sc * hi[e], pre[e]);
+  } else {
+    const int c0 = (blockIdx.x * 64 + lane) * 4;
+    const bool ok = c0 < g.N;
+    const int cf = ok ? c0 : 0;
+    typename Epi::Pre pre[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pre[e] = epi.fetch(row, cf + e);
+    const f32x4 t = sum_splits(g, row, cf);
+    float ss = 0.f;
+    if (ok) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += epi.one(row, c0 + e, sc * t[e], pre[e]);
     }
     if constexpr (Epi::kSsq) {
-#pragma unroll
-      for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
-      if (ok && q == 0) epi.ssq(row, blockIdx.x, ss);
+      ss = wave_sum(ss);
+      if (lane == 0) epi.ssq(row, blockIdx.x, ss);
     }
   }
 }

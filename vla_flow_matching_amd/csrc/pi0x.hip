@@ -67,6 +67,12 @@ pi0x_status fail(pi0x_status s, const std::string& msg) {
 
 constexpr int kMaxGraphs = 32;
 constexpr size_t kGemmPartialFloats = (size_t)16 << 20;  // split-K partial tiles (float32 path)
+// Attention key splits: used while fewer than kAttnSplitMinBlocks 128-query
+// tiles exist; at most kAttnPartialBlocks split blocks per launch.
+constexpr int kAttnSplitMinBlocks = 128;
+constexpr int kAttnPartialBlocks = 256;
+// Key counts are padded to 64 (the bf16 key block; float32 uses 32).
+inline int prefix_pad(int L) { return ((L > 0 ? L : 1) + 63) / 64 * 64; }
 constexpr int kCounters = 1 << 16;
 
 struct Layer {
@@ -101,11 +107,12 @@ struct pi0x_expert {
   std::vector<void*> allocs;
   std::vector<Layer> layers;
   void *w_tt = nullptr, *w_mo = nullptr;  // time half of action_time_mlp_in, action_time_mlp_out
-  float* w_comb = nullptr;  // [W][A] action half of action_time_mlp_in times action_in_proj
+  float* w_comb = nullptr;  // [A][W] (W_mi,a W_in)^T: action half of action_time_mlp_in times action_in_proj
   void* w_outp = nullptr;   // [Apad][W] action_out_proj, columns scaled by (1 + final_norm), rows >= A zero
   int Apad = 0;
   float *b_mi = nullptr, *b_mo = nullptr, *w_s = nullptr, *b_s = nullptr, *b_out = nullptr;
-  float *rope_cos = nullptr, *rope_sin = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;  // [position][head_dim/2]
+  float2* rope_cs = nullptr;                        // per call: (cos, sin) of every suffix row [R][head_dim/2]
   float* hs = nullptr;  // state tokens of the call [B][W]
   float* hbuf = nullptr;  // residual stream [R][W] float32
   void* hb = nullptr;     // bf16 copy of the residual stream (bf16 mode)
@@ -114,6 +121,9 @@ struct pi0x_expert {
   void *vts = nullptr, *vtp = nullptr;  // suffix / prefix values, transposed
   float *x = nullptr, *tbias = nullptr;
   float* gemm_partial = nullptr;
+  float* stream_partial = nullptr;  // K-split partial tiles of the M <= 64 bf16 GEMMs
+  size_t stream_partial_n = 0;
+  float* attn_partial = nullptr;  // split attention states [blocks][2 + head_dim/4][512]
   unsigned* gemm_counters = nullptr;
   CallDesc* desc = nullptr;
   hipStream_t cap_stream = nullptr;
@@ -201,7 +211,7 @@ struct Timed {
 // Column-group width of the sum-of-squares partials a residual producer writes
 // for M rows (the wave or block width of the kernel launch_gemm picks for it).
 int producer_group(bool bf16, int M) {
-  if (bf16) return M <= 64 ? 16 : 64;
+  if (bf16) return M <= 64 ? kStreamGroup : 64;
   return M <= 1024 ? 32 : 64;
 }
 
@@ -259,9 +269,30 @@ pi0x_status launch_gemm_big(hipStream_t s, GemmArgs g, const Epi& epi) {
   return PI0X_OK;
 }
 
-template <int BN, class Epi>
-pi0x_status launch_gemm_skinny(hipStream_t s, GemmArgs g, const Epi& epi) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<BN, Epi>), dim3(g.N / BN), dim3(512), 0, s, g, epi);
+template <int NW, int TN, class Epi>
+pi0x_status launch_gemm_wide(hipStream_t s, GemmArgs g, const Epi& epi) {
+  gemm_wide_kernel<NW, TN, Epi><<<dim3(g.N / (16 * TN)), dim3(NW * 64), 0, s>>>(g, epi);
+  PI0X_HIP(hipGetLastError());
+  return PI0X_OK;
+}
+
+// K slice of one stream block: 256 when it divides K, else 128 or 64.
+inline int stream_kb(int K) { return K % 256 == 0 ? 256 : (K % 128 == 0 ? 128 : 64); }
+inline size_t stream_partial_floats(int K, int N) { return (size_t)(K / stream_kb(K)) * 64 * N; }
+
+template <class Epi>
+pi0x_status launch_gemm_stream(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi& epi) {
+  const int KB = stream_kb(g.K);
+  g.splits = g.K / KB;
+  g.partial = h->stream_partial;
+  if ((size_t)g.splits * g.M * g.N > h->stream_partial_n) return fail(PI0X_ERR_SHAPE, "stream GEMM partials exceed the workspace");
+  const dim3 grid(g.N / 64, g.splits);
+  if (KB == 256) gemm_stream_kernel<256><<<grid, dim3(256), 0, s>>>(g);
+  else if (KB == 128) gemm_stream_kernel<128><<<grid, dim3(256), 0, s>>>(g);
+  else gemm_stream_kernel<64><<<grid, dim3(256), 0, s>>>(g);
+  PI0X_HIP(hipGetLastError());
+  const int cols = Epi::kPaired ? 512 : kStreamGroup;
+  gemm_reduce_kernel<Epi><<<dim3((g.N + cols - 1) / cols, g.M), dim3(64), 0, s>>>(g, epi);
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
 }
@@ -276,13 +307,15 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
   const GemmArgs g = make_args(h, A, lda, W, M, N, K, nin);
   if constexpr (sizeof(T) == 2) {
     if (M <= 64) {
-      if constexpr (Epi::kSsq) {
-        return launch_gemm_skinny<16>(s, g, epi);
-      } else if constexpr (Epi::kPaired) {
-        return N / 64 >= 128 ? launch_gemm_skinny<64>(s, g, epi) : launch_gemm_skinny<32>(s, g, epi);
-      } else {
-        return N / 32 >= 128 ? launch_gemm_skinny<32>(s, g, epi) : launch_gemm_skinny<16>(s, g, epi);
+      // one kernel for the wide paired projection (gate/up): N alone fills the
+      // chip, and a wave's K share fits its registers
+      if constexpr (Epi::kPaired) {
+        if (N % 32 == 0 && N / 32 >= 128) {
+          if (K <= 2048 && K % 512 == 0) return launch_gemm_wide<8, 2>(s, g, epi);
+          if (K <= 1024 && K % 256 == 0) return launch_gemm_wide<4, 2>(s, g, epi);
+        }
       }
+      return launch_gemm_stream(h, s, g, epi);
     }
     if (N % 128 == 0) return launch_gemm_big<128, 128>(s, g, epi);
     return fail(PI0X_ERR_SHAPE, "bf16 GEMM with more than 64 rows needs N % 128 == 0");
@@ -315,9 +348,19 @@ pi0x_status allow_big_smem_all() {
 // ---------------------------------------------------------------------------
 // Attention dispatch
 // ---------------------------------------------------------------------------
+// Key blocks of one split: large batches fill the chip with 128-query tiles
+// alone; small ones divide each sample's key blocks over gridDim.z and merge
+// the splits in attn_combine_kernel.
+inline int attn_splits(int B, int tiles, int nblk) {
+  if (B * tiles >= kAttnSplitMinBlocks) return 1;
+  int sp = std::min(nblk, kAttnPartialBlocks / (B * tiles));
+  return std::max(sp, 1);
+}
+
 template <typename T, int DH>
 pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer) {
-  const int Lp = round_up(L > 0 ? L : 1, 32);
+  constexpr int KB = AttnCfg<T>::KB;
+  const int Lp = prefix_pad(L);
   AttnArgs a;
   a.qk = h->qk;
   a.ldqk = h->qd + DH;
@@ -336,13 +379,36 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   a.ldo = h->qd;
   a.scale = 1.0f / std::sqrt((float)DH);
   const int nq = h->nh * h->S;
-  if (B * ((nq + 63) / 64) >= 128) {
-    hipLaunchKernelGGL((attn_kernel<T, DH>), dim3((nq + 63) / 64, B), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attn_small_kernel<T, DH>), dim3((nq + 15) / 16, B), dim3(512), 0, s, a);
-  }
+  const int tiles = (nq + 127) / 128;
+  const int nblk = (L + KB - 1) / KB + (h->S + KB - 1) / KB;
+  a.splits = attn_splits(B, tiles, nblk);
+  a.partial = h->attn_partial;
+  constexpr size_t smem = attn_smem_bytes<T, DH>();
+  attn_kernel<T, DH><<<dim3(tiles, B, a.splits), dim3(512), smem, s>>>(a);
   PI0X_HIP(hipGetLastError());
+  if (a.splits > 1) {
+    attn_combine_kernel<T, DH><<<dim3(tiles, B, attn_combine_chunks<DH>()), dim3(512), 0, s>>>(a);
+    PI0X_HIP(hipGetLastError());
+  }
   return PI0X_OK;
+}
+
+template <typename T, int DH>
+pi0x_status allow_attn_smem_dh() {
+  PI0X_HIP(hipFuncSetAttribute((const void*)attn_kernel<T, DH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)attn_smem_bytes<T, DH>()));
+  return PI0X_OK;
+}
+
+template <typename T>
+pi0x_status allow_attn_smem(int dh) {
+  switch (dh) {
+    case 32: return allow_attn_smem_dh<T, 32>();
+    case 64: return allow_attn_smem_dh<T, 64>();
+    case 128: return allow_attn_smem_dh<T, 128>();
+    case 256: return allow_attn_smem_dh<T, 256>();
+  }
+  return fail(PI0X_ERR_SHAPE, "unsupported head_dim");
 }
 
 template <typename T>
@@ -359,7 +425,7 @@ pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer) 
 template <typename T>
 pi0x_status launch_transpose_v(pi0x_expert* h, hipStream_t s, int B, int L) {
   if (L <= 0) return PI0X_OK;
-  const int Lp = round_up(L, 32);
+  const int Lp = prefix_pad(L);
   hipLaunchKernelGGL((transpose_v_kernel<T>), dim3(Lp / 32, (h->dh + 63) / 64, h->D * B), dim3(256), 0, s, h->desc, B,
                      L, h->dh, Lp, reinterpret_cast<T*>(h->vtp));
   PI0X_HIP(hipGetLastError());
@@ -403,7 +469,14 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
     return PI0X_OK;
   };
   PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, state_tok());
-  const int nA = (AR + 15) / 16;
+  auto rope_rows = [&]() -> pi0x_status {
+    hipLaunchKernelGGL(rope_rows_kernel, dim3(R), dim3(128), 0, s, h->desc, S, L, h->dh / 2, h->rope_cos, h->rope_sin,
+                       h->rope_cs);
+    PI0X_HIP(hipGetLastError());
+    return PI0X_OK;
+  };
+  PI0X_TIMED(PI0X_KERNEL_QKV_ROPE, rope_rows());
+  const int nA = (AR + 3) / 4 * ((W + 255) / 256);
   for (int k = 0; k < steps; ++k) {
     const int first = (k == 0);
     auto suffix_in = [&]() -> pi0x_status {
@@ -420,8 +493,8 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
       const Layer& ly = h->layers[l];
       PI0X_TIMED(PI0X_KERNEL_QKV_ROPE,
                  (launch_gemm<T>(h, s, hA, W, ly.wqkv, R, h->nqkv, W,
-                                 EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, L, h->desc,
-                                               h->rope_cos, h->rope_sin, (T*)h->vts, h->Sp},
+                                 EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, h->rope_cs,
+                                               (T*)h->vts, h->Sp},
                                  nin)));
       PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l));
       PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
@@ -625,7 +698,7 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
         for (int a = 0; a < A; ++a) acc[a] += wk * wik[a];
         bacc += wk * bin[k];
       }
-      for (int a = 0; a < A; ++a) comb[(size_t)o * A + a] = (float)acc[a];
+      for (int a = 0; a < A; ++a) comb[(size_t)a * W + o] = (float)acc[a];
       bmi2[o] = (float)bacc;
     }
     PI0X_TRY(h->allocT(&h->w_comb, comb.size() * sizeof(float)));
@@ -666,8 +739,8 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
   h->W = cfg->width; h->D = cfg->depth; h->M = cfg->mlp_dim; h->nh = cfg->num_heads; h->dh = cfg->head_dim;
   h->H = cfg->action_horizon; h->A = cfg->action_dim; h->Sd = cfg->state_dim; h->S = h->H + 1;
   h->qd = h->nh * h->dh; h->nqkv = h->qd + 2 * h->dh; h->Bmax = cfg->max_batch; h->Lmax = cfg->max_prefix_len;
-  h->Lpmax = round_up(h->Lmax > 0 ? h->Lmax : 1, 32);
-  h->Sp = round_up(h->S, 32);
+  h->Lpmax = prefix_pad(h->Lmax);
+  h->Sp = round_up(h->S, 64);
   const float* blob = static_cast<const float*>(weights_host);
   if (h->bf16()) PI0X_TRY(upload_weights<uint16_t>(h, blob));
   else PI0X_TRY(upload_weights<float>(h, blob));
@@ -687,6 +760,12 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
   PI0X_TRY(h->allocT(&h->x, AR * h->A * 4));
   PI0X_TRY(h->alloc(&h->tau, (size_t)cfg->max_steps * h->W * e));
   PI0X_TRY(h->allocT(&h->tbias, (size_t)cfg->max_steps * h->W * 4));
+  if (h->bf16()) {
+    const int shapes[][2] = {{h->W, h->W}, {h->W, h->nqkv}, {h->qd, h->W}, {h->W, 2 * h->M}, {h->M, h->W}, {h->W, h->Apad}};
+    for (const auto& kn : shapes) h->stream_partial_n = std::max(h->stream_partial_n, stream_partial_floats(kn[0], kn[1]));
+    PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
+  }
+  PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
   if (!h->bf16()) {
     PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
     PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
@@ -697,12 +776,15 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
   const int P = h->Lmax + h->S + 1;
   PI0X_TRY(h->allocT(&h->rope_cos, (size_t)P * (h->dh / 2) * 4));
   PI0X_TRY(h->allocT(&h->rope_sin, (size_t)P * (h->dh / 2) * 4));
+  PI0X_TRY(h->allocT(&h->rope_cs, (size_t)h->Bmax * h->S * (h->dh / 2) * sizeof(float2)));
   const int n = P * (h->dh / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, P, h->dh, (double)cfg->rope_theta,
                      h->rope_cos, h->rope_sin);
   PI0X_HIP(hipGetLastError());
   PI0X_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
   if (h->bf16()) PI0X_TRY(allow_big_smem_all());
+  if (h->bf16()) PI0X_TRY(allow_attn_smem<bf16>(h->dh));
+  else PI0X_TRY(allow_attn_smem<float>(h->dh));
   PI0X_HIP(hipDeviceSynchronize());
   return PI0X_OK;
 }

@@ -36,44 +36,46 @@ __global__ __launch_bounds__(256) void state_token_kernel(const CallDesc* __rest
 }
 
 // Suffix-embedding input of one Euler step (page 1, embed_suffix).
-// Blocks < nA: 16 action rows each.  action_in_proj is folded into the action
-// half of action_time_mlp_in at create time (w_comb = W_mi,a W_in, and
-// W_mi,a b_in is part of the step bias cb), so the first layer of the time MLP
-// is u = SiLU(w_comb x + cb) with K = action_dim; u goes to the model dtype.
-// Blocks >= nA: copy the state token of one sample into hidden row b*S
-// (float32, its bf16 copy in bf16 mode, and its sum-of-squares partials over
-// groups of G columns).  x comes from desc->x_in when from_input, else from
-// the loop's own x buffer.
+// action_in_proj is folded into the action half of action_time_mlp_in at create
+// time (w_comb = W_mi,a W_in, and W_mi,a b_in is part of the step bias cb), so
+// the first layer of the time MLP is u = SiLU(w_comb x + cb) with K =
+// action_dim; u goes to the model dtype.  w_comb is stored transposed,
+// wt[a][o].  Blocks < nA: 256 outputs o of RB action rows each (block id =
+// row block * nchunks + output chunk).  Blocks >= nA: copy the state token of
+// one sample into hidden row b*S (float32, its bf16 copy in bf16 mode, and its
+// sum-of-squares partials over groups of G columns, G <= 256).  x comes from
+// desc->x_in when from_input, else from the loop's own x buffer.
 template <typename T>
 __global__ __launch_bounds__(256) void suffix_in_kernel(const CallDesc* __restrict__ desc, const float* x_loop,
                                                         int from_input, int AR, int nA, int A, int W, int S,
-                                                        const float* __restrict__ w_comb, const float* __restrict__ cb,
+                                                        const float* __restrict__ wt, const float* __restrict__ cb,
                                                         T* __restrict__ u, const float* __restrict__ hs,
                                                         float* __restrict__ hbuf, T* __restrict__ hb,
                                                         float* __restrict__ ssq, int G) {
-  constexpr int RB = 16;
+  constexpr int RB = 4;
   __shared__ float xs[RB][64];
   if ((int)blockIdx.x < nA) {
-    const int r0 = blockIdx.x * RB;
+    const int nchunks = (W + 255) / 256;
+    const int r0 = (blockIdx.x / nchunks) * RB, o = (blockIdx.x % nchunks) * 256 + threadIdx.x;
     const float* xsrc = from_input ? desc->x_in : x_loop;
     for (int i = threadIdx.x; i < RB * 64; i += 256) {
       const int rr = i / 64, a = i - rr * 64;
       xs[rr][a] = (r0 + rr < AR && a < A) ? xsrc[(size_t)(r0 + rr) * A + a] : 0.f;
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < W; o += 256) {
-      float wr[64];
+    if (o >= W) return;
+    float acc[RB];
+    const float bias = cb[o];
 #pragma unroll
-      for (int a = 0; a < 64; ++a) wr[a] = a < A ? w_comb[(size_t)o * A + a] : 0.f;
-      const float bias = cb[o];
+    for (int rr = 0; rr < RB; ++rr) acc[rr] = bias;
+    for (int a = 0; a < A; ++a) {
+      const float w = wt[(size_t)a * W + o];
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        float acc = bias;
-#pragma unroll
-        for (int a = 0; a < 64; ++a) acc += wr[a] * xs[rr][a];
-        if (r0 + rr < AR) u[(size_t)(r0 + rr) * W + o] = from_f32<T>(silu(acc));
-      }
+      for (int rr = 0; rr < RB; ++rr) acc[rr] += w * xs[rr][a];
     }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+      if (r0 + rr < AR) u[(size_t)(r0 + rr) * W + o] = from_f32<T>(silu(acc[rr]));
     return;
   }
   const int b = blockIdx.x - nA;
@@ -113,6 +115,18 @@ __global__ void time_features_kernel(const CallDesc* __restrict__ desc, int N, i
     tau[(size_t)k * W + j] = from_f32<T>((float)sin(arg));
     tau[(size_t)k * W + half + j] = from_f32<T>((float)cos(arg));
   }
+}
+
+// (cos, sin) of every suffix row of the call: row b*S + s sits at position
+// valid_len[b] + s (valid_len clamped to [0, L]); cs[row][j] from the tables.
+__global__ __launch_bounds__(128) void rope_rows_kernel(const CallDesc* __restrict__ desc, int S, int L, int half,
+                                                        const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                                                        float2* __restrict__ cs) {
+  const int row = blockIdx.x, b = row / S, s = row - b * S;
+  int v = desc->valid[b];
+  v = v < 0 ? 0 : (v > L ? L : v);
+  const size_t p = (size_t)(v + s) * half;
+  for (int j = threadIdx.x; j < half; j += 128) cs[(size_t)row * half + j] = float2{cos_t[p + j], sin_t[p + j]};
 }
 
 // Rotary table for positions 0..P-1: theta = p * base^(-2j/d), j < d/2,
