@@ -74,6 +74,34 @@ def kernel_unit_counts(shape, batch: int, esz: int, valid: np.ndarray):
     }
 
 
+def csrc_digest() -> str:
+    """sha256 over the HIP sources and the C header, to tell whether kernel code
+    changed since HBM byte counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vla_flow_matching_amd", "csrc")
+    for p in sorted(os.listdir(csrc)) + ["../../include/pi0x.h"]:
+        with open(os.path.join(csrc, p), "rb") as f:
+            h.update(p.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (already scaled by the copy-kernel
+    calibration), or None when absent or taken on different kernel code."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = table.get(workload, {}).get(kernel)
+    if not e or e.get("csrc_sha256") != csrc_digest():
+        return None
+    return float(e["bytes_per_launch"])
+
+
 def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
     import torch
     from vla_flow_matching_amd import binding, synth
@@ -131,7 +159,7 @@ def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
         peak = MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS
         roof = {"bound": "mfma", "achieved": u["flops"] / avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(name, dom)
     roof["kernel"] = dom
     roof["per_launch"] = {"bytes": u["bytes"], "flops": u["flops"], "avg_us": kern[dom]["avg_us"]}
     sec = ms * 1e-3
@@ -176,6 +204,9 @@ def main():
     ap.add_argument("--workload", default="pi0_bf16_b64")
     ap.add_argument("--b1-workload", default="pi0_bf16_b1", help="secondary latency workload ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a known-size reference "
+                         "kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the denoise loop shards by "
@@ -184,6 +215,13 @@ def main():
 
     import torch
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     main_res = run_workload(args.workload, args.steps, args.warmup)
     w = main_res["workload"]
     line = {
