@@ -7,10 +7,10 @@
 //  * gemm_kernel      16x16 tiles, bf16 or fp32 operands (fp32 through eight
 //                     v_mfma_f32_16x16x4_f32 per 32-wide K slice): the float32
 //                     path and the fallback for any shape.
-//  * gemm_big_kernel  bf16, v_mfma_f32_32x32x16_bf16, 128x128 or 256x256
-//                     block tiles with 2x2 waves of 64x64 / 128x128 and K
-//                     slices of 64 double-buffered through padded LDS: the
-//                     compute-bound shapes (batch >= 2).
+//  * gemm_tile_kernel bf16, v_mfma_f32_32x32x16_bf16, 128x128 block tiles of
+//                     2x2 waves, K slices DMA'd straight into an LDS ring,
+//                     XCD-aware tile order: the compute-bound shapes (more
+//                     than 64 rows, i.e. batch >= 2).
 //  * gemm_wide_kernel  bf16, M <= 64, wide N (batch 1): one block per 16-32
 //                     columns over the whole K range, all loads in flight at
 //                     once, epilogue in the same kernel.
@@ -415,58 +415,122 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, Epi epi) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// gemm_big_kernel: bf16, 32x32x16 MFMA, 2x2 waves, K slices of 64
-// ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-template <int BM, int BN>
-constexpr size_t big_smem_bytes() {
-  return (size_t)2 * (BM + BN) * (64 + 8) * 2;
+// ---------------------------------------------------------------------------
+// gemm_tile_kernel: bf16, 32x32x16 MFMA, NWM x NWN waves of (BM/NWM) x (BN/NWN),
+// K slices of BK moved straight from global memory into an LDS ring of ST
+// stages (global_load_lds_dwordx4, no register staging), so the loads of the
+// next ST-1 slices are in flight while a slice feeds the matrix cores.  LDS
+// rows are BK bf16 with the 16-byte chunks of row r stored at position
+// chunk ^ ((r / RPS) % CPR) (CPR chunks per row, RPS rows per 256 bytes): the
+// 16 rows one fragment read serves at a time then cover all 64 banks once,
+// with no padding (the DMA writes 64 consecutive 16-byte slots per wave).
+// One barrier per slice: a wave waits for its own loads of slice k, the
+// barrier makes everyone's visible, and only then is slice k+ST-1 issued into
+// the buffer slice k-1 used.
+//
+// Tile order: the blocks are dealt round-robin to the 8 XCDs (block L runs on
+// XCD L % 8), so block L takes tile t = (L % 8) * ceil(T/8) + L / 8 -- each XCD
+// owns a contiguous run of tiles -- and tiles run in groups of group_m row
+// tiles by all column tiles, so the blocks resident on one XCD share their A
+// row panels and W column panels in that XCD's L2.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int ST>
+constexpr size_t tile_smem_bytes() {
+  return (size_t)ST * (BM + BN) * BK * 2;
 }
 
-template <int BM, int BN, class Epi>
-__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, Epi epi) {
-  constexpr int BK = 64, LDK = BK + 8;  // 144-byte LDS rows: conflict-free 16-byte fragment reads
-  constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;
-  constexpr int CPR = BK / 8;  // 16-byte chunks per row
-  constexpr int AC = BM * CPR / 256, BC = BN * CPR / 256;
-  constexpr int ELD = TN * 32 + 1;  // epilogue staging row (floats)
-  static_assert(AC >= 1 && BC >= 1 && BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "tile/thread mismatch");
-  static_assert(4 * 32 * ELD * 4 <= (int)big_smem_bytes<BM, BN>(), "epilogue staging must fit");
+__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for
+// every outstanding global load (its fence covers the DMA writes), draining
+// the prefetch; the ring orders its DMA with explicit vmcnt waits instead, and
+// the empty asm statements only keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most `ahead` ring stages of PER loads each are outstanding.
+template <int PER, int ST>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  if (ST >= 4 && ahead >= 2) wait_vmcnt<(ST >= 4 ? 2 * PER : 0)>();
+  else if (ST >= 3 && ahead >= 1) wait_vmcnt<(ST >= 3 ? PER : 0)>();
+  else wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
+__global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n,
+                                                                   int group_m) {
+  constexpr int NT = NWM * NWN * 64;
+  constexpr int TM = BM / NWM / 32, TN = BN / NWN / 32;
+  constexpr int CPR = BK / 8, RPS = 256 / (BK * 2);  // 16-byte chunks per row, rows per 256 bytes
+  constexpr int STAGE = (BM + BN) * BK;               // bf16 elements per ring stage
+  constexpr int AJ = BM * CPR / NT, BJ = BN * CPR / NT;  // DMA chunks per thread per stage
+  constexpr int ELD = TN * 32 + 1;                    // epilogue staging row (floats)
+  static_assert(BK == 32 || BK == 64, "slice width");
+  static_assert(AJ >= 1 && BJ >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert((size_t)(NT / 64) * 32 * ELD * 4 <= tile_smem_bytes<BM, BN, BK, ST>(), "epilogue staging must fit");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* As = reinterpret_cast<bf16*>(smem_raw);  // [2][BM*LDK]
-  bf16* Bs = As + 2 * BM * LDK;                   // [2][BN*LDK]
+  bf16* ring = reinterpret_cast<bf16*>(smem_raw);
   __shared__ float s_inv[BM];
 
+  // tile of this block
+  const int T = tiles_m * tiles_n, per_xcd = (T + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (t >= T) return;
+  const int gsize = group_m * tiles_n, grp = t / gsize, first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m), within = t - grp * gsize;
+  const int m_tile = first_m + within % gm, n_tile = within / gm;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n_tile = blockIdx.x, m_tile = blockIdx.y;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int KI = g.K / BK;
   const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
 
-  // staging: thread t moves 16-byte chunks t, t+256, ... of each operand tile
-  // rows past M load row M-1 (unconditional loads keep the pipeline free of
-  // waits); their results are never stored
-  const bf16* aptr[AC];
-  int aoff[AC];
+  // DMA sources: slot (wave*J + j)*64 + lane of a stage holds row slot / CPR,
+  // chunk (slot % CPR) ^ swizzle(row); rows past M repeat row M-1 (never stored)
+  const bf16* asrc[AJ];
 #pragma unroll
-  for (int i = 0; i < AC; ++i) {
-    const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * 8;
-    aptr[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + kc;
-    aoff[i] = row * LDK + kc;
+  for (int j = 0; j < AJ; ++j) {
+    const int slot = (wave * AJ + j) * 64 + lane, row = slot / CPR, c = (slot % CPR) ^ ((row / RPS) % CPR);
+    asrc[j] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + c * 8;
   }
-  const bf16* bptr[BC];
-  int boff[BC];
+  const bf16* bsrc[BJ];
 #pragma unroll
-  for (int i = 0; i < BC; ++i) {
-    const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * 8;
-    bptr[i] = W + (size_t)(n0 + row) * g.ldw + kc;
-    boff[i] = row * LDK + kc;
+  for (int j = 0; j < BJ; ++j) {
+    const int slot = (wave * BJ + j) * 64 + lane, row = slot / CPR, c = (slot % CPR) ^ ((row / RPS) % CPR);
+    bsrc[j] = W + (size_t)(n0 + row) * g.ldw + c * 8;
   }
-  u32x4 ra[AC], rb[BC];
+  auto issue = [&](int kt) {
+    bf16* sa = ring + (kt % ST) * STAGE;
+    bf16* sb = sa + BM * BK;
+    const int ko = kt * BK;
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) lds_dma16(asrc[j] + ko, sa + (wave * AJ + j) * 512);
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) lds_dma16(bsrc[j] + ko, sb + (wave * BJ + j) * 512);
+  };
+
+  if constexpr (Epi::kRowScale) row_scale_prologue(g, m0, BM, s_inv);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -476,62 +540,43 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, Epi epi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if constexpr (Epi::kRowScale) row_scale_prologue(g, m0, BM, s_inv);
 #pragma unroll
-  for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i]);
-#pragma unroll
-  for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i]);
-#pragma unroll
-  for (int i = 0; i < AC; ++i) *reinterpret_cast<u32x4*>(&As[aoff[i]]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < BC; ++i) *reinterpret_cast<u32x4*>(&Bs[boff[i]]) = rb[i];
-  __syncthreads();
-  int st = 0;
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < KI) issue(p);
+  // fragment rows: lane % 32 of each 32-row MFMA tile (tile bases are multiples of 32)
+  const int fr = lane & 31, fh = lane >> 5, sw = (fr / RPS) % CPR;
   for (int kt = 0; kt < KI; ++kt) {
-    const bool more = kt + 1 < KI;
-    if (more) {
-      const int ko = (kt + 1) * BK;
-#pragma unroll
-      for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + ko);
-#pragma unroll
-      for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + ko);
-    }
-    const bf16* as = As + st * BM * LDK + (wm * TM * 32 + fr) * LDK + fk;
-    const bf16* bs = Bs + st * BN * LDK + (wn * TN * 32 + fr) * LDK + fk;
+    wait_stages<AJ + BJ, ST>(min(ST - 2, KI - 1 - kt));  // later slices may stay in flight
+    ring_barrier();
+    if (kt + ST - 1 < KI) issue(kt + ST - 1);
+    const bf16* sa = ring + (kt % ST) * STAGE + (wm * TM * 32 + fr) * BK;
+    const bf16* sb = ring + (kt % ST) * STAGE + BM * BK + (wn * TN * 32 + fr) * BK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
+      const int pos = ((kk * 2 + fh) ^ sw) * 8;
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LDK + kk * 16);
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sa + i * 32 * BK + pos);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LDK + kk * 16);
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sb + j * 32 * BK + pos);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    // keep the stores of the next slice (and their wait on its global loads)
-    // after the matrix-core work, so the loads overlap the MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      bf16* as_n = As + (st ^ 1) * BM * LDK;
-      bf16* bs_n = Bs + (st ^ 1) * BN * LDK;
-#pragma unroll
-      for (int i = 0; i < AC; ++i) *reinterpret_cast<u32x4*>(&as_n[aoff[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < BC; ++i) *reinterpret_cast<u32x4*>(&bs_n[boff[i]]) = rb[i];
-    }
-    __syncthreads();
-    st ^= 1;
   }
+  // every wave is done reading the ring before it is reused for the epilogue
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // Epilogue through LDS, one 32-row strip of the wave tile at a time: the
   // strip is written in the MFMA layout (element (i, j, v) is row
   // 8 (v/4) + 4 (lane/32) + v%4, column 32 j + lane % 32 of the strip) and read
   // back row-wise, so the epilogue loops index no accumulator dynamically.
-  // Lanes cover LPR items of a row and RPI rows at a time; the reads of 8 such
-  // row groups are issued before their stores.
+  // Lanes cover LPR items of a row and RPI rows at a time; the reads of GP such
+  // row groups are issued before their stores.  Residual producers put each
+  // element's h^2 back into the strip and sum the strip's rows afterwards
+  // (two lanes per row), instead of a cross-lane reduction per row.
   float* strip = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
   const int mb = m0 + wm * TM * 32, nb = n0 + wn * TN * 32;
   constexpr int WC = TN * 32;                            // wave tile width
@@ -569,7 +614,6 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, Epi epi) {
         const int row = mb + i * 32 + r;
         const bool ok = row < g.M;
         const float sc = Epi::kRowScale ? s_inv[min(row, g.M - 1) - m0] : 1.f;
-        float ss = 0.f;
 #pragma unroll
         for (int q = 0; q < IPL; ++q) {
           const int it = lc + q * LPR;
@@ -577,15 +621,24 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, Epi epi) {
             const int c = (it >> 4) * 32 + (it & 15);
             if (ok) epi.pair(row, nb + c, sc * strip[r * ELD + c], sc * strip[r * ELD + c + 16], pre[pp][q]);
           } else {
-            if (ok) ss += epi.one(row, nb + it, sc * strip[r * ELD + it], pre[pp][q]);
+            const float sq = ok ? epi.one(row, nb + it, sc * strip[r * ELD + it], pre[pp][q]) : 0.f;
+            if constexpr (Epi::kSsq) strip[r * ELD + it] = sq;
           }
         }
-        if constexpr (Epi::kSsq) {
-#pragma unroll
-          for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
-          if (ok && lc == 0) epi.ssq(row, nb / WC, ss);
-        }
       }
+    }
+    if constexpr (Epi::kSsq) {
+      // the strip now holds this wave's h^2; lanes 2r and 2r+1 sum row r.  The
+      // lanes of one wave access LDS in program order; the asm statement keeps
+      // the compiler from moving the reads above the other lanes' writes.
+      asm volatile("" ::: "memory");
+      const int r = lane >> 1, h0 = (lane & 1) * (WC / 2);
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < WC / 2; ++c) ss += strip[r * ELD + h0 + c];
+      ss += __shfl_xor(ss, 1, 64);
+      const int row = mb + i * 32 + r;
+      if ((lane & 1) == 0 && row < g.M) epi.ssq(row, nb / WC, ss);
     }
     __syncthreads();
   }

@@ -260,13 +260,25 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi
   return PI0X_OK;
 }
 
-template <int BM, int BN, class Epi>
-pi0x_status launch_gemm_big(hipStream_t s, GemmArgs g, const Epi& epi) {
-  dim3 grid(g.N / BN, (g.M + BM - 1) / BM, 1);
-  constexpr size_t smem = big_smem_bytes<BM, BN>();
-  gemm_big_kernel<BM, BN, Epi><<<grid, dim3(256), smem, s>>>(g, epi);
+// Tile kernel configurations: wide N (several tiles per CU) streams K in
+// slices of 32 through a 3-stage ring (48 KB of LDS, 3 blocks per CU); narrow
+// N (about one tile per CU, long K) uses slices of 64 double-buffered (64 KB,
+// 2 blocks per CU).
+template <int BK, int ST, class Epi>
+pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
+  constexpr int BM = 128, BN = 128;
+  const int tm = (g.M + BM - 1) / BM, tn = g.N / BN;
+  const int blocks = 8 * ((tm * tn + 7) / 8);
+  constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST>();
+  gemm_tile_kernel<BM, BN, BK, ST, 2, 2, Epi><<<dim3(blocks), dim3(256), smem, s>>>(g, epi, tm, tn, 8);
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
+}
+
+template <class Epi>
+pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
+  if (g.N >= 2048) return launch_gemm_tile_cfg<32, 3>(s, g, epi);
+  return launch_gemm_tile_cfg<64, 2>(s, g, epi);
 }
 
 template <int NW, int TN, class Epi>
@@ -317,7 +329,7 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
       }
       return launch_gemm_stream(h, s, g, epi);
     }
-    if (N % 128 == 0) return launch_gemm_big<128, 128>(s, g, epi);
+    if (N % 128 == 0) return launch_gemm_tile(s, g, epi);
     return fail(PI0X_ERR_SHAPE, "bf16 GEMM with more than 64 rows needs N % 128 == 0");
   } else {
     if (M > 1024 && N % 128 == 0) return launch_gemm_cfg<T, 128, 128, 2, 2>(h, s, g, epi);
@@ -328,20 +340,22 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
 
 // Kernels that take more than 64 KiB of dynamic LDS must opt in once.
 template <class Epi>
-pi0x_status allow_big_smem() {
-  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_big_kernel<128, 128, Epi>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)big_smem_bytes<128, 128>()));
+pi0x_status allow_tile_smem() {
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 128, 32, 3, 2, 2, Epi>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 32, 3>()));
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 128, 64, 2, 2, 2, Epi>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 64, 2>()));
   return PI0X_OK;
 }
 
-pi0x_status allow_big_smem_all() {
-  PI0X_TRY(allow_big_smem<EpiStore<float>>());
-  PI0X_TRY(allow_big_smem<EpiStore<bf16>>());
-  PI0X_TRY(allow_big_smem<EpiSuffixRows<bf16>>());
-  PI0X_TRY(allow_big_smem<EpiResidual<bf16>>());
-  PI0X_TRY(allow_big_smem<EpiQkvRope<bf16>>());
-  PI0X_TRY(allow_big_smem<EpiGeglu<bf16>>());
-  PI0X_TRY(allow_big_smem<EpiEuler>());
+pi0x_status allow_tile_smem_all() {
+  PI0X_TRY(allow_tile_smem<EpiStore<float>>());
+  PI0X_TRY(allow_tile_smem<EpiStore<bf16>>());
+  PI0X_TRY(allow_tile_smem<EpiSuffixRows<bf16>>());
+  PI0X_TRY(allow_tile_smem<EpiResidual<bf16>>());
+  PI0X_TRY(allow_tile_smem<EpiQkvRope<bf16>>());
+  PI0X_TRY(allow_tile_smem<EpiGeglu<bf16>>());
+  PI0X_TRY(allow_tile_smem<EpiEuler>());
   return PI0X_OK;
 }
 
@@ -782,7 +796,7 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
                      h->rope_cos, h->rope_sin);
   PI0X_HIP(hipGetLastError());
   PI0X_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
-  if (h->bf16()) PI0X_TRY(allow_big_smem_all());
+  if (h->bf16()) PI0X_TRY(allow_tile_smem_all());
   if (h->bf16()) PI0X_TRY(allow_attn_smem<bf16>(h->dh));
   else PI0X_TRY(allow_attn_smem<float>(h->dh));
   PI0X_HIP(hipDeviceSynchronize());
