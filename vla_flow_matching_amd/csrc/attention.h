@@ -18,9 +18,15 @@
 // q/k/v projection.  Masked keys get probability exactly 0; padded prefix keys
 // are never read from the caller's cache (zeros are used instead).
 //
-// With splits > 1 (small batches) the key blocks of a sample are divided over
-// gridDim.z; each split writes its running max, sum and unnormalised output
-// and attn_combine_kernel merges them in split order.
+// With splits > 1 (small batches) the key blocks of a sample are divided into
+// splits; each split writes its running max, sum and unnormalised output and
+// attn_combine_kernel merges them in split order.
+//
+// Block order: the grid is 1-D and blocks are dealt round-robin to the 8 XCDs
+// (block L runs on XCD L % 8).  Work unit u = (b * splits + split) * tiles +
+// tile goes to block (u / per_xcd) + 8 * (u % per_xcd), per_xcd = ceil(units
+// / 8): each XCD takes a contiguous run of units, so the query tiles that read
+// the same keys run together on one XCD and share them in its L2.
 #pragma once
 
 #include "common.h"
@@ -40,7 +46,7 @@ struct AttnArgs {
   void* out;  // [B*S][ldo], head n of token s at column n*head_dim
   int ldo;
   float scale;
-  int splits;
+  int splits, tiles;
   float* partial;  // splits > 1: [B][tiles][splits][2 + head_dim/4][512]
 };
 
@@ -75,7 +81,10 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   T* Vt = Ks + 2 * KB * LDK;               // [2][DH * LDV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int units = a.B * a.splits * a.tiles, per_xcd = (units + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (u >= units) return;
+  const int tile = u % a.tiles, split = (u / a.tiles) % a.splits, b = u / (a.tiles * a.splits);
   const int nq = a.nh * a.S;
   const int qi = tile * 128 + wave * 16 + (lane & 15);
   const bool qok = qi < nq;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (a.splits > 1) {
     constexpr int NR = 2 + ND * 4;
-    float* mine = a.partial + (((size_t)b * gridDim.x + tile) * a.splits + split) * NR * 512;
+    float* mine = a.partial + (((size_t)b * a.tiles + tile) * a.splits + split) * NR * 512;
     mine[tid] = m_run;
     mine[512 + tid] = l_tot;
 #pragma unroll
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
   const int qi = tile * 128 + wave * 16 + (lane & 15);
   if (qi >= nq) return;
   const int qs = qi / a.nh, qn = qi - qs * a.nh;
-  const float* P = a.partial + ((size_t)b * gridDim.x + tile) * a.splits * NR * 512 + tid;
+  const float* P = a.partial + ((size_t)b * a.tiles + tile) * a.splits * NR * 512 + tid;
   float mz = -INFINITY;
 #pragma unroll 8
   for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * NR * 512]);

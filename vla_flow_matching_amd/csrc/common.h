@@ -92,6 +92,25 @@ __device__ __forceinline__ void load4x2(Frag<float>& f, const float* p0, const f
 __device__ __forceinline__ void set_frag(Frag<bf16>& f, int i, float x) { f.v[i] = f2bf(x); }
 __device__ __forceinline__ void set_frag(Frag<float>& f, int i, float x) { f.v[i] = x; }
 
+// 8 consecutive floats from memory (two 16-byte loads) / to memory as T
+// (one 16-byte store for bf16, two for float32).  Pointers 16-byte aligned.
+__device__ __forceinline__ void load8f(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(bf16* p, const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = f2bf(v[i]);
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

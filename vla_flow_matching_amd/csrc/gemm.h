@@ -7,7 +7,7 @@
 //  * gemm_kernel      16x16 tiles, bf16 or fp32 operands (fp32 through eight
 //                     v_mfma_f32_16x16x4_f32 per 32-wide K slice): the float32
 //                     path and the fallback for any shape.
-//  * gemm_tile_kernel bf16, v_mfma_f32_32x32x16_bf16, 128x128 block tiles of
+//  * gemm_tile_kernel bf16, v_mfma_f32_16x16x32_bf16, 128x128 block tiles of
 //                     2x2 waves, K slices DMA'd straight into an LDS ring,
 //                     XCD-aware tile order: the compute-bound shapes (more
 //                     than 64 rows, i.e. batch >= 2).
@@ -67,8 +67,14 @@ struct GemmArgs {
 // < M.  Each epilogue splits its global reads into fetch(row, col) -> Pre, so
 // the kernels can issue the reads of a group of rows before any of the group's
 // stores (the compiler cannot move a read past a store that may alias it).
+// The *8 forms do the same for 8 consecutive columns col .. col+7 (col % 8 ==
+// 0; for pairs col % 32 < 16 and the partners are col+16 .. col+23), with
+// 16-byte loads and stores.
 // ---------------------------------------------------------------------------
 struct NoPre {};
+struct Pre8f {
+  float v[8];
+};
 
 // out[row][col] = act(x + bias[col]) in TO; act = SiLU when silu != 0.
 template <typename TO>
@@ -84,6 +90,25 @@ struct EpiStore {
     float v = x + b;
     if (silu) v = pi0x::silu(v);
     out[(size_t)row * ldo + col] = from_f32<TO>(v);
+    return 0.f;
+  }
+  using Pre8 = Pre8f;
+  __device__ __forceinline__ Pre8 fetch8(int, int col) const {
+    Pre8 b;
+    if (bias) load8f(bias + col, b.v);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b.v[e] = 0.f;
+    return b;
+  }
+  __device__ __forceinline__ float one8(int row, int col, const float* x, const Pre8& b) const {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = x[e] + b.v[e];
+      if (silu) v[e] = pi0x::silu(v[e]);
+    }
+    store8(out + (size_t)row * ldo + col, v);
     return 0.f;
   }
   __device__ __forceinline__ void ssq(int, int, float) const {}
@@ -111,6 +136,24 @@ struct EpiSuffixRows {
     if (hb) hb[i] = from_f32<TB>(v);
     return v * v;
   }
+  using Pre8 = Pre8f;
+  __device__ __forceinline__ Pre8 fetch8(int, int col) const {
+    Pre8 b;
+    load8f(bias + col, b.v);
+    return b;
+  }
+  __device__ __forceinline__ float one8(int row, int col, const float* x, const Pre8& b) const {
+    const size_t i = (size_t)hrow(row) * ldh + col;
+    float v[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = x[e] + b.v[e];
+      ss += v[e] * v[e];
+    }
+    store8(h + i, v);
+    if (hb) store8(hb + i, v);
+    return ss;
+  }
   __device__ __forceinline__ void ssq(int row, int group, float s) const { ssq_out[(size_t)hrow(row) * np + group] = s; }
 };
 
@@ -132,6 +175,24 @@ struct EpiResidual {
     h[i] = v;
     if (hb) hb[i] = from_f32<TB>(v);
     return v * v;
+  }
+  using Pre8 = Pre8f;
+  __device__ __forceinline__ Pre8 fetch8(int row, int col) const {
+    Pre8 o;
+    load8f(h + (size_t)row * ldh + col, o.v);
+    return o;
+  }
+  __device__ __forceinline__ float one8(int row, int col, const float* x, const Pre8& old) const {
+    const size_t i = (size_t)row * ldh + col;
+    float v[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = old.v[e] + x[e];
+      ss += v[e] * v[e];
+    }
+    store8(h + i, v);
+    if (hb) store8(hb + i, v);
+    return ss;
   }
   __device__ __forceinline__ void ssq(int row, int group, float s) const { ssq_out[(size_t)row * np + group] = s; }
 };
@@ -174,6 +235,47 @@ struct EpiQkvRope {
       o[(size_t)16 * vt_ld] = from_f32<T>(x2);
     }
   }
+  struct Pre8 {
+    float2 cs[8];
+  };
+  __device__ __forceinline__ Pre8 fetch8(int row, int c) const {
+    Pre8 p;
+    if (c < qk_cols) {
+      const float4* src = reinterpret_cast<const float4*>(cs + (size_t)row * (head_dim >> 1) + jj(c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 t = src[e];
+        p.cs[2 * e] = float2{t.x, t.y};
+        p.cs[2 * e + 1] = float2{t.z, t.w};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p.cs[e] = float2{0.f, 0.f};
+    }
+    return p;
+  }
+  __device__ __forceinline__ void pair8(int row, int c, const float* x1, const float* x2, const Pre8& p) const {
+    if (c < qk_cols) {
+      const int half = head_dim >> 1;
+      T* o = out + (size_t)row * ldo + (c / head_dim) * head_dim + jj(c);
+      float r1[8], r2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        r1[e] = x1[e] * p.cs[e].x - x2[e] * p.cs[e].y;
+        r2[e] = x2[e] * p.cs[e].x + x1[e] * p.cs[e].y;
+      }
+      store8(o, r1);
+      store8(o + half, r2);
+    } else {
+      const int b = row / S, s = row - b * S;
+      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + s;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[(size_t)e * vt_ld] = from_f32<T>(x1[e]);
+        o[(size_t)(16 + e) * vt_ld] = from_f32<T>(x2[e]);
+      }
+    }
+  }
 };
 
 // GeGLU epilogue (after the inv_rms row scale): stored column c (gate of hidden
@@ -187,6 +289,14 @@ struct EpiGeglu {
   __device__ __forceinline__ Pre fetch(int, int) const { return NoPre{}; }
   __device__ __forceinline__ void pair(int row, int c, float g, float u, Pre) const {
     out[(size_t)row * ldo + (c >> 5) * 16 + (c & 15)] = from_f32<T>(gelu_tanh_fast<T>(g) * u);
+  }
+  using Pre8 = NoPre;
+  __device__ __forceinline__ Pre8 fetch8(int, int) const { return NoPre{}; }
+  __device__ __forceinline__ void pair8(int row, int c, const float* g, const float* u, const Pre8&) const {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_fast<T>(g[e]) * u[e];
+    store8(out + (size_t)row * ldo + (c >> 5) * 16 + (c & 15), v);
   }
 };
 
@@ -226,6 +336,18 @@ struct EpiEuler {
       x_loop[i] = xn;
       if (write_out) desc->out[i] = xn;
     }
+    return 0.f;
+  }
+  using Pre8 = Pre8f;
+  __device__ __forceinline__ Pre8 fetch8(int row, int col) const {
+    Pre8 p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p.v[e] = fetch(row, col + e);
+    return p;
+  }
+  __device__ __forceinline__ float one8(int row, int col, const float* acc, const Pre8& p) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) one(row, col + e, acc[e], p.v[e]);
     return 0.f;
   }
   __device__ __forceinline__ void ssq(int, int, float) const {}
@@ -415,10 +537,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, Epi epi) {
   }
 }
 
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-
 // ---------------------------------------------------------------------------
-// gemm_tile_kernel: bf16, 32x32x16 MFMA, NWM x NWN waves of (BM/NWM) x (BN/NWN),
+// gemm_tile_kernel: bf16, 16x16x32 MFMA, NWM x NWN waves of (BM/NWM) x (BN/NWN)
+// (4x4 tiles per wave at 128x128: sixteen independent accumulator chains),
 // K slices of BK moved straight from global memory into an LDS ring of ST
 // stages (global_load_lds_dwordx4, no register staging), so the loads of the
 // next ST-1 slices are in flight while a slice feeds the matrix cores.  LDS
@@ -438,7 +559,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int ST>
 constexpr size_t tile_smem_bytes() {
-  return (size_t)ST * (BM + BN) * BK * 2;
+  // the ring, or the epilogue strips of the 4 waves (32 rows x (BN/2 + 4) floats), whichever is larger
+  return (size_t)ST * (BM + BN) * BK * 2 > (size_t)4 * 32 * (BN / 2 + 4) * 4 ? (size_t)ST * (BM + BN) * BK * 2
+                                                                             : (size_t)4 * 32 * (BN / 2 + 4) * 4;
 }
 
 __device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
@@ -478,14 +601,14 @@ template <int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n,
                                                                    int group_m) {
   constexpr int NT = NWM * NWN * 64;
-  constexpr int TM = BM / NWM / 32, TN = BN / NWN / 32;
+  constexpr int TM = BM / NWM / 16, TN = BN / NWN / 16;  // 16x16 MFMA tiles per wave
   constexpr int CPR = BK / 8, RPS = 256 / (BK * 2);  // 16-byte chunks per row, rows per 256 bytes
   constexpr int STAGE = (BM + BN) * BK;               // bf16 elements per ring stage
   constexpr int AJ = BM * CPR / NT, BJ = BN * CPR / NT;  // DMA chunks per thread per stage
-  constexpr int ELD = TN * 32 + 1;                    // epilogue staging row (floats)
+  constexpr int ELD = TN * 16 + 4;                    // epilogue staging row (floats, 16-byte aligned)
   static_assert(BK == 32 || BK == 64, "slice width");
   static_assert(AJ >= 1 && BJ >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
-  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(TM % 2 == 0 && TN >= 1, "wave tile: 32-row strips of 16x16 tiles");
   static_assert((size_t)(NT / 64) * 32 * ELD * 4 <= tile_smem_bytes<BM, BN, BK, ST>(), "epilogue staging must fit");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* ring = reinterpret_cast<bf16*>(smem_raw);
@@ -532,113 +655,99 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
 
   if constexpr (Epi::kRowScale) row_scale_prologue(g, m0, BM, s_inv);
 
-  f32x16 acc[TM][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p)
     if (p < KI) issue(p);
-  // fragment rows: lane % 32 of each 32-row MFMA tile (tile bases are multiples of 32)
-  const int fr = lane & 31, fh = lane >> 5, sw = (fr / RPS) % CPR;
+  // fragment rows: lane % 16 of each 16-row MFMA tile (tile bases are multiples of 16),
+  // K chunk 4*kk + lane/16 of the slice
+  const int fr = lane & 15, fq = lane >> 4, sw = (fr / RPS) % CPR;
   for (int kt = 0; kt < KI; ++kt) {
     wait_stages<AJ + BJ, ST>(min(ST - 2, KI - 1 - kt));  // later slices may stay in flight
     ring_barrier();
     if (kt + ST - 1 < KI) issue(kt + ST - 1);
-    const bf16* sa = ring + (kt % ST) * STAGE + (wm * TM * 32 + fr) * BK;
-    const bf16* sb = ring + (kt % ST) * STAGE + BM * BK + (wn * TN * 32 + fr) * BK;
+    const bf16* sa = ring + (kt % ST) * STAGE + (wm * TM * 16 + fr) * BK;
+    const bf16* sb = ring + (kt % ST) * STAGE + BM * BK + (wn * TN * 16 + fr) * BK;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int pos = ((kk * 2 + fh) ^ sw) * 8;
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const int pos = ((kk * 4 + fq) ^ sw) * 8;
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sa + i * 32 * BK + pos);
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sa + i * 16 * BK + pos);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sb + j * 32 * BK + pos);
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sb + j * 16 * BK + pos);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
   // every wave is done reading the ring before it is reused for the epilogue
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Epilogue through LDS, one 32-row strip of the wave tile at a time: the
-  // strip is written in the MFMA layout (element (i, j, v) is row
-  // 8 (v/4) + 4 (lane/32) + v%4, column 32 j + lane % 32 of the strip) and read
-  // back row-wise, so the epilogue loops index no accumulator dynamically.
-  // Lanes cover LPR items of a row and RPI rows at a time; the reads of GP such
-  // row groups are issued before their stores.  Residual producers put each
-  // element's h^2 back into the strip and sum the strip's rows afterwards
-  // (two lanes per row), instead of a cross-lane reduction per row.
+  // Epilogue through LDS, one 32-row strip (two 16-row MFMA tiles) of the wave
+  // tile at a time: the strip is written in the MFMA layout (element e of tile
+  // (ii, j) is row 16 ii + 4 (lane/16) + e, column 16 j + lane % 16) and read
+  // back as 8 consecutive columns of one row per lane, so every global access
+  // of the epilogue is 16 bytes or more.  Non-paired: CH = WC/8 lanes per row;
+  // paired: one lane takes columns c .. c+7 and their partners c+16 .. c+23.
+  // All fetches of the strip are issued before its stores.  Residual
+  // producers sum h^2 over the CH lanes of a row.
   float* strip = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
-  const int mb = m0 + wm * TM * 32, nb = n0 + wn * TN * 32;
-  constexpr int WC = TN * 32;                            // wave tile width
-  constexpr int PPR = Epi::kPaired ? WC / 2 : WC;        // items per row
-  constexpr int LPR = PPR < 64 ? PPR : 64;               // lanes per row
-  constexpr int RPI = 64 / LPR;                          // rows per pass
-  constexpr int IPL = PPR / LPR;                         // items per lane and row
-  constexpr int NP = 32 / RPI;                           // passes per strip
-  constexpr int GP = NP < 8 ? NP : 8;                    // passes per read group
-  const int lr = lane / LPR, lc = lane % LPR;
+  const int mb = m0 + wm * TM * 16, nb = n0 + wn * TN * 16;
+  constexpr int WC = TN * 16;                        // wave tile width
+  constexpr int CH = Epi::kPaired ? WC / 16 : WC / 8;  // lanes per row
+  constexpr int RPP = 64 / CH;                       // rows per pass
+  constexpr int NPASS = 32 / RPP;                    // passes per strip
+  static_assert(WC % 32 == 0 && 64 % CH == 0 && 32 % RPP == 0, "epilogue lane layout");
+  const int rin = lane / CH, q = lane % CH;
+  const int c = Epi::kPaired ? (q >> 1) * 32 + (q & 1) * 8 : q * 8;  // first column of this lane's chunk
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM / 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        strip[((v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * ELD + j * 32 + (lane & 31)] = acc[i][j][v];
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          strip[(ii * 16 + (lane >> 4) * 4 + e) * ELD + j * 16 + (lane & 15)] = acc[2 * i + ii][j][e];
     __syncthreads();
+    typename Epi::Pre8 pre[NPASS];
 #pragma unroll
-    for (int p0 = 0; p0 < NP; p0 += GP) {
-      typename Epi::Pre pre[GP][IPL];
-#pragma unroll
-      for (int pp = 0; pp < GP; ++pp) {
-        const int row = min(mb + i * 32 + (p0 + pp) * RPI + lr, g.M - 1);
-#pragma unroll
-        for (int q = 0; q < IPL; ++q) {
-          const int it = lc + q * LPR;
-          const int c = Epi::kPaired ? (it >> 4) * 32 + (it & 15) : it;
-          pre[pp][q] = epi.fetch(row, nb + c);
-        }
-      }
-#pragma unroll
-      for (int pp = 0; pp < GP; ++pp) {
-        const int r = (p0 + pp) * RPI + lr;
-        const int row = mb + i * 32 + r;
-        const bool ok = row < g.M;
-        const float sc = Epi::kRowScale ? s_inv[min(row, g.M - 1) - m0] : 1.f;
-#pragma unroll
-        for (int q = 0; q < IPL; ++q) {
-          const int it = lc + q * LPR;
-          if constexpr (Epi::kPaired) {
-            const int c = (it >> 4) * 32 + (it & 15);
-            if (ok) epi.pair(row, nb + c, sc * strip[r * ELD + c], sc * strip[r * ELD + c + 16], pre[pp][q]);
-          } else {
-            const float sq = ok ? epi.one(row, nb + it, sc * strip[r * ELD + it], pre[pp][q]) : 0.f;
-            if constexpr (Epi::kSsq) strip[r * ELD + it] = sq;
-          }
-        }
-      }
+    for (int p = 0; p < NPASS; ++p) {
+      const int row = min(mb + i * 32 + p * RPP + rin, g.M - 1);
+      pre[p] = epi.fetch8(row, nb + c);
     }
-    if constexpr (Epi::kSsq) {
-      // the strip now holds this wave's h^2; lanes 2r and 2r+1 sum row r.  The
-      // lanes of one wave access LDS in program order; the asm statement keeps
-      // the compiler from moving the reads above the other lanes' writes.
-      asm volatile("" ::: "memory");
-      const int r = lane >> 1, h0 = (lane & 1) * (WC / 2);
-      float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < WC / 2; ++c) ss += strip[r * ELD + h0 + c];
-      ss += __shfl_xor(ss, 1, 64);
+    for (int p = 0; p < NPASS; ++p) {
+      const int r = p * RPP + rin;
       const int row = mb + i * 32 + r;
-      if ((lane & 1) == 0 && row < g.M) epi.ssq(row, nb / WC, ss);
+      const bool ok = row < g.M;
+      const float sc = Epi::kRowScale ? s_inv[min(row, g.M - 1) - m0] : 1.f;
+      float lo[8];
+      load8f(strip + r * ELD + c, lo);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo[e] *= sc;
+      if constexpr (Epi::kPaired) {
+        float hi[8];
+        load8f(strip + r * ELD + c + 16, hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hi[e] *= sc;
+        if (ok) epi.pair8(row, nb + c, lo, hi, pre[p]);
+      } else {
+        float ss = ok ? epi.one8(row, nb + c, lo, pre[p]) : 0.f;
+        if constexpr (Epi::kSsq) {
+#pragma unroll
+          for (int off = 1; off < CH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+          if (ok && q == 0) epi.ssq(row, nb / WC, ss);
+        }
+      }
     }
     __syncthreads();
   }

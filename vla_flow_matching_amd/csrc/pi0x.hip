@@ -260,10 +260,8 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi
   return PI0X_OK;
 }
 
-// Tile kernel configurations: wide N (several tiles per CU) streams K in
-// slices of 32 through a 3-stage ring (48 KB of LDS, 3 blocks per CU); narrow
-// N (about one tile per CU, long K) uses slices of 64 double-buffered (64 KB,
-// 2 blocks per CU).
+// Tile kernel configuration: 128x128 tiles, K slices of 64 double-buffered
+// (64 KB of LDS, 2 blocks per CU).
 template <int BK, int ST, class Epi>
 pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
   constexpr int BM = 128, BN = 128;
@@ -277,7 +275,6 @@ pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
 
 template <class Epi>
 pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
-  if (g.N >= 2048) return launch_gemm_tile_cfg<32, 3>(s, g, epi);
   return launch_gemm_tile_cfg<64, 2>(s, g, epi);
 }
 
@@ -341,8 +338,6 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
 // Kernels that take more than 64 KiB of dynamic LDS must opt in once.
 template <class Epi>
 pi0x_status allow_tile_smem() {
-  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 128, 32, 3, 2, 2, Epi>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 32, 3>()));
   PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 128, 64, 2, 2, 2, Epi>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 64, 2>()));
   return PI0X_OK;
@@ -396,9 +391,11 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   const int tiles = (nq + 127) / 128;
   const int nblk = (L + KB - 1) / KB + (h->S + KB - 1) / KB;
   a.splits = attn_splits(B, tiles, nblk);
+  a.tiles = tiles;
   a.partial = h->attn_partial;
   constexpr size_t smem = attn_smem_bytes<T, DH>();
-  attn_kernel<T, DH><<<dim3(tiles, B, a.splits), dim3(512), smem, s>>>(a);
+  const int units = B * a.splits * tiles;
+  attn_kernel<T, DH><<<dim3(8 * ((units + 7) / 8)), dim3(512), smem, s>>>(a);
   PI0X_HIP(hipGetLastError());
   if (a.splits > 1) {
     attn_combine_kernel<T, DH><<<dim3(tiles, B, attn_combine_chunks<DH>()), dim3(512), 0, s>>>(a);
