@@ -6,11 +6,10 @@
 // shared by all query heads, so the num_heads * S queries of a sample (query
 // index qi = s*num_heads + n) form one matrix against one key/value sequence.
 //
-// attn_kernel: a block of 8 waves owns 128 queries (16 per wave).  Keys are
-// staged in blocks of KB (64 for bf16, 32 for fp32): K row-major and V
-// transposed ([head_dim][keys]) are copied into LDS with 16-byte accesses and
-// shared by the 8 waves, double-buffered so the global loads of block i+1
-// overlap the matrix-core work on block i.  A wave computes S^T = K Q^T, so a
+// attn_kernel: a block owns 128 queries (8 waves of 16).  Keys are staged in blocks of KB (64 for bf16, 32 for fp32): K
+// row-major and V transposed ([head_dim][keys]) are copied into LDS with
+// 16-byte accesses and shared by the waves, double-buffered so the global
+// loads of block i+1 overlap the matrix-core work on block i.  A wave computes S^T = K Q^T, so a
 // lane holds the scores of its own query (lane % 16); the online softmax runs
 // in float32 in registers and O^T = V^T P^T reuses those probabilities
 // directly as the MFMA operand.  The prefix values are transposed once per
@@ -47,12 +46,18 @@ struct AttnArgs {
   int ldo;
   float scale;
   int splits, tiles;
-  float* partial;  // splits > 1: [B][tiles][splits][2 + head_dim/4][512]
+  float* partial;  // splits > 1: [B][tiles][splits][QT][2 + head_dim/4][threads], 512 per (query tile, field)
 };
 
+// Per dtype: KB keys per staged block, NW waves per block, QT 16-query tiles
+// per wave (NW * QT * 16 = 128 queries per block).  Two query tiles per wave
+// (4 waves) halve the LDS fragment reads per query but need about 440
+// registers per lane at head_dim 256 and measured slower than 8 waves of one
+// tile, which is what both dtypes use.
 template <typename T> struct AttnCfg;
-template <> struct AttnCfg<bf16> { static constexpr int KB = 64; };
-template <> struct AttnCfg<float> { static constexpr int KB = 32; };
+template <> struct AttnCfg<bf16> { static constexpr int KB = 64, NW = 8, QT = 1; };
+template <> struct AttnCfg<float> { static constexpr int KB = 32, NW = 8, QT = 1; };
+constexpr int kAttnQueries = 128;  // queries per block
 
 template <typename T, int DH>
 constexpr size_t attn_smem_bytes() {
@@ -65,8 +70,9 @@ template <typename T> __device__ __forceinline__ float fexp(float x) { return ex
 template <> __device__ __forceinline__ float fexp<bf16>(float x) { return __expf(x); }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
-  constexpr int KB = AttnCfg<T>::KB;
+__global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
+  constexpr int KB = AttnCfg<T>::KB, NW = AttnCfg<T>::NW, QT = AttnCfg<T>::QT, NT = NW * 64;
+  static_assert(NW * QT * 16 == kAttnQueries, "queries per block");
   constexpr int KT = KB / 16;   // 16-key score tiles per block
   constexpr int KS = KB / 32;   // 32-key PV steps per block
   constexpr int VE = 16 / (int)sizeof(T);
@@ -74,8 +80,8 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   constexpr int LDV = KB + VE;  // padded V^T row
   constexpr int NC = DH / 32, ND = DH / 16;
   constexpr int NVEC = KB * DH / VE;        // 16-byte vectors of K (and of V^T) per key block
-  constexpr int KVEC = (NVEC + 511) / 512;  // per thread
-  constexpr bool FULL = NVEC % 512 == 0;
+  constexpr int KVEC = (NVEC + NT - 1) / NT;  // per thread
+  constexpr bool FULL = NVEC % NT == 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   T* Ks = reinterpret_cast<T*>(smem_raw);  // [2][KB * LDK]
   T* Vt = Ks + 2 * KB * LDK;               // [2][DH * LDV]
@@ -86,9 +92,15 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   if (u >= units) return;
   const int tile = u % a.tiles, split = (u / a.tiles) % a.splits, b = u / (a.tiles * a.splits);
   const int nq = a.nh * a.S;
-  const int qi = tile * 128 + wave * 16 + (lane & 15);
-  const bool qok = qi < nq;
-  const int qs = qok ? qi / a.nh : 0, qn = qok ? qi - qs * a.nh : 0;
+  int qs[QT], qn[QT];
+  bool qok[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int qi = tile * kAttnQueries + (wave * QT + t) * 16 + (lane & 15);
+    qok[t] = qi < nq;
+    qs[t] = qok[t] ? qi / a.nh : 0;
+    qn[t] = qok[t] ? qi - qs[t] * a.nh : 0;
+  }
 
   // uniform over the block: keeps the key-block loop in scalar registers
   int valid = __builtin_amdgcn_readfirstlane(a.desc->valid[b]);
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     kzero = 0;
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = tid + i * 512, kk = v / (DH / VE), dc = v % (DH / VE), key = base + kk;
+      const int v = tid + i * NT, kk = v / (DH / VE), dc = v % (DH / VE), key = base + kk;
       if (!FULL && v >= NVEC) break;
       const T* src = pre ? Kp + (size_t)min(key, max(lim - 1, 0)) * DH : Sq + (size_t)min(key, lim - 1) * a.ldqk + a.col_k;
       rk[i] = gload16(src + dc * VE);
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = tid + i * 512, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
+      const int v = tid + i * NT, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
       if (!FULL && v >= NVEC) break;
       const T* src = pre ? Vtp + (size_t)d * a.Lp + base + kc : Vts + (size_t)d * a.Sp + base + kc;
       rv[i] = gload16(src);
@@ -133,33 +145,42 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     T* vt = Vt + st * DH * LDV;
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = tid + i * 512, kk = v / (DH / VE), dc = v % (DH / VE);
+      const int v = tid + i * NT, kk = v / (DH / VE), dc = v % (DH / VE);
       if (!FULL && v >= NVEC) break;
       *reinterpret_cast<u32x4*>(&ks[kk * LDK + dc * VE]) = ((kzero >> i) & 1u) ? u32x4{0u, 0u, 0u, 0u} : rk[i];
     }
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = tid + i * 512, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
+      const int v = tid + i * NT, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
       if (!FULL && v >= NVEC) break;
       *reinterpret_cast<u32x4*>(&vt[d * LDV + kc]) = rv[i];
     }
   };
 
-  Frag<T> qf[NC];
-  {
-    const T* qrow = Sq + (size_t)qs * a.ldqk + qn * DH;
+  Frag<T> qf[QT][NC];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const T* qrow = Sq + (size_t)qs[t] * a.ldqk + qn[t] * DH;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (qok) load8(qf[c], qrow + c * 32 + g * 8);
+      if (qok[t]) load8(qf[t][c], qrow + c * 32 + g * 8);
       else
 #pragma unroll
-        for (int i = 0; i < 8; ++i) set_frag(qf[c], i, 0.f);
+        for (int i = 0; i < 8; ++i) set_frag(qf[t][c], i, 0.f);
     }
   }
-  f32x4 o[ND];
+  f32x4 o[QT][ND];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;  // running max (same on the 4 lanes of a query), this lane's share of the sum
+  for (int t = 0; t < QT; ++t)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max (same on the 4 lanes of a query) and this lane's share of the sum, per query tile
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
 
   // unconditional (an empty split stages a block it never reads) so that
   // every path into the loop has waited for all loads issued so far
@@ -176,57 +197,69 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     const int base = pre ? blk * KB : (blk - nb_pre) * KB;
     const int lim = pre ? valid : a.S;
 
-    // scores: lane holds its query vs key kt*16 + 4g + e of the block
-    float s[KT][4];
+    // scores: lane holds query tile t's query (lane % 16) vs key kt*16 + 4g + e of the block
+    float sc[QT][KT][4];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[QT];
+#pragma unroll
+      for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         Frag<T> kf;
         load8(kf, &ks[(kt * 16 + (lane & 15)) * LDK + c * 32 + g * 8]);
-        mma32(kf, qf[c], acc);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = base + kt * 16 + g * 4 + e;
-        bool vis = key < lim;
-        if (!pre) vis = vis && (qs >= 1 || key == 0);
-        s[kt][e] = vis ? acc[e] * a.scale : -INFINITY;
-      }
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = base + kt * 16 + g * 4 + e;
+          bool vis = key < lim;
+          if (!pre) vis = vis && (qs[t] >= 1 || key == 0);
+          sc[t][kt][e] = vis ? acc[t][e] * a.scale : -INFINITY;
+        }
     }
-    float bmax = -INFINITY;
+    float m_new[QT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int t = 0; t < QT; ++t) {
+      float bmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, s[kt][e]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fexp<T>(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      o[d][0] *= alpha; o[d][1] *= alpha; o[d][2] *= alpha; o[d][3] *= alpha;
+        for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sc[t][kt][e]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      m_new[t] = fmaxf(m_run[t], bmax);
+      const float alpha = (m_new[t] == -INFINITY) ? 1.f : fexp<T>(m_run[t] - m_new[t]);
+      l_run[t] *= alpha;
+      m_run[t] = m_new[t];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        o[t][d][0] *= alpha; o[t][d][1] *= alpha; o[t][d][2] *= alpha; o[t][d][3] *= alpha;
+      }
     }
 #pragma unroll
     for (int ks2 = 0; ks2 < KS; ++ks2) {
       // probabilities of keys 32*ks2 + (i/4)*16 + 4g + i%4 as the PV operand
-      Frag<T> pf;
+      Frag<T> pf[QT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = s[2 * ks2 + i / 4][i % 4];
-        const float e = (x == -INFINITY) ? 0.f : fexp<T>(x - m_new);
-        l_run += e;
-        set_frag(pf, i, e);
-      }
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = sc[t][2 * ks2 + i / 4][i % 4];
+          const float e = (x == -INFINITY) ? 0.f : fexp<T>(x - m_new[t]);
+          l_run[t] += e;
+          set_frag(pf[t], i, e);
+        }
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         Frag<T> vf;
         const T* vrow = &vt[(d * 16 + (lane & 15)) * LDV + ks2 * 32];
         load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
-        mma32(vf, pf, o[d]);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) mma32(vf, pf[t], o[t][d]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -234,72 +267,73 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
     st ^= 1;
   }
 
-  // lane holds O[q][d*16 + 4g + e] (unnormalised); total softmax denominator of its query
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (a.splits > 1) {
-    constexpr int NR = 2 + ND * 4;
-    float* mine = a.partial + (((size_t)b * a.tiles + tile) * a.splits + split) * NR * 512;
-    mine[tid] = m_run;
-    mine[512 + tid] = l_tot;
+  // lane holds O[q][d*16 + 4g + e] (unnormalised) of its query in each tile
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    float l_tot = l_run[t] + __shfl_xor(l_run[t], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (a.splits > 1) {
+      constexpr int NR = 2 + ND * 4;
+      float* mine = a.partial + (((size_t)b * a.tiles + tile) * a.splits + split) * (QT * NR * NT) + (size_t)t * NR * NT;
+      mine[tid] = m_run[t];
+      mine[NT + tid] = l_tot;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[(2 + d * 4 + e) * NT + tid] = o[t][d][e];
+      continue;
+    }
+    if (!qok[t]) continue;
+    const float inv = 1.f / l_tot;
+    T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs[t]) * a.ldo + qn[t] * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mine[(2 + d * 4 + e) * 512 + tid] = o[d][e];
-    return;
+      for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(o[t][d][e] * inv);
   }
-  if (!qok) return;
-  const float inv = 1.f / l_tot;
-  T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
-#pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) orow[d * 16 + g * 4 + e] = from_f32<T>(o[d][e] * inv);
 }
 
 // Merges the split partial softmax states of attn_kernel in split order.
-// Grid (tiles, B, head_dim / 16): thread tid of the block takes the query
-// that thread tid of attn_kernel held and the 4 output features of d-tile
-// blockIdx.z it held there.
-template <int DH> constexpr int attn_combine_dc() { return 1; }
+// Grid (tiles, B, head_dim / 16), 512 threads: slot s = QT-tile t * NT +
+// thread of attn_kernel (the query and the lanes it held there), 4 output
+// features of d-tile blockIdx.z.
 template <int DH> constexpr int attn_combine_chunks() { return DH / 16; }
 
 template <typename T, int DH>
 __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
-  constexpr int ND = DH / 16, NR = 2 + ND * 4, DC = attn_combine_dc<DH>(), NV = DC * 4;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * DC;
+  constexpr int NW = AttnCfg<T>::NW, QT = AttnCfg<T>::QT, NT = NW * 64;
+  constexpr int ND = DH / 16, NR = 2 + ND * 4;
+  static_assert(QT * NT == 512, "one combine thread per attention slot");
+  const int slot = threadIdx.x, t = slot / NT, tid = slot % NT;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int tile = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z;
   const int nq = a.nh * a.S;
-  const int qi = tile * 128 + wave * 16 + (lane & 15);
+  const int qi = tile * kAttnQueries + (wave * QT + t) * 16 + (lane & 15);
   if (qi >= nq) return;
   const int qs = qi / a.nh, qn = qi - qs * a.nh;
-  const float* P = a.partial + ((size_t)b * a.tiles + tile) * a.splits * NR * 512 + tid;
+  const float* P = a.partial + ((size_t)b * a.tiles + tile) * a.splits * (QT * NR * NT) + (size_t)t * NR * NT + tid;
   float mz = -INFINITY;
 #pragma unroll 8
-  for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * NR * 512]);
+  for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * QT * NR * NT]);
   float l = 0.f;
-  float o[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) o[i] = 0.f;
-#pragma unroll 2
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int z = 0; z < a.splits; ++z) {
-    const float* pz = P + (size_t)z * NR * 512;
-    float v[2 + NV];
+    const float* pz = P + (size_t)z * QT * NR * NT;
+    float v[6];
     v[0] = pz[0];
-    v[1] = pz[512];
+    v[1] = pz[NT];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[2 + i] = pz[(2 + d0 * 4 + i) * 512];
+    for (int e = 0; e < 4; ++e) v[2 + e] = pz[(2 + d0 * 4 + e) * NT];
     const float w = (v[0] == -INFINITY) ? 0.f : fexp<T>(v[0] - mz);
     l += w * v[1];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) o[i] += w * v[2 + i];
+    for (int e = 0; e < 4; ++e) o[e] += w * v[2 + e];
   }
   const float inv = 1.f / l;
   T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
-  for (int d = 0; d < DC; ++d)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) orow[(d0 + d) * 16 + g * 4 + e] = from_f32<T>(o[d * 4 + e] * inv);
+  for (int e = 0; e < 4; ++e) orow[d0 * 16 + g * 4 + e] = from_f32<T>(o[e] * inv);
 }
 
 // Prefix values, transposed once per call: vt[l][b][d][Lp] = V_l[b][key][d] for

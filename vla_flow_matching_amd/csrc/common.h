@@ -121,11 +121,13 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // tanh-GELU through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)):
 // gelu(x) = x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3))).  The bf16 path
-// uses the hardware exp2, the float32 path libm expf.
+// uses the hardware exp2 and reciprocal (its result is rounded to bf16), the
+// float32 path libm expf and an IEEE division.
 template <typename T>
 __device__ __forceinline__ float gelu_tanh_fast(float x) {
   const float u = -1.5957691216057308f * (x + 0.044715f * x * x * x);  // -2 sqrt(2/pi) (...)
-  return x / (1.0f + (sizeof(T) == 2 ? __expf(u) : expf(u)));
+  if (sizeof(T) == 2) return x * __builtin_amdgcn_rcpf(1.0f + __expf(u));  // v_rcp_f32 (1 ulp)
+  return x / (1.0f + expf(u));
 }
 
 }  // namespace pi0x

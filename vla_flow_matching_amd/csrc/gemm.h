@@ -588,6 +588,11 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Orders one wave's LDS accesses across lanes: a wave's LDS instructions
+// execute in program order, so only the compiler has to be kept from moving
+// loads and stores across this point.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
+
 // Waits until at most `ahead` ring stages of PER loads each are outstanding.
 template <int PER, int ST>
 __device__ __forceinline__ void wait_stages(int ahead) {
@@ -653,6 +658,10 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
     for (int j = 0; j < BJ; ++j) lds_dma16(bsrc[j] + ko, sb + (wave * BJ + j) * 512);
   };
 
+  // the first slices go out before anything waits on memory
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < KI) issue(p);
   if constexpr (Epi::kRowScale) row_scale_prologue(g, m0, BM, s_inv);
 
   f32x4 acc[TM][TN];
@@ -660,10 +669,6 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int p = 0; p < ST - 1; ++p)
-    if (p < KI) issue(p);
   // fragment rows: lane % 16 of each 16-row MFMA tile (tile bases are multiples of 16),
   // K chunk 4*kk + lane/16 of the slice
   const int fr = lane & 15, fq = lane >> 4, sw = (fr / RPS) % CPR;
@@ -698,7 +703,10 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
   // of the epilogue is 16 bytes or more.  Non-paired: CH = WC/8 lanes per row;
   // paired: one lane takes columns c .. c+7 and their partners c+16 .. c+23.
   // All fetches of the strip are issued before its stores.  Residual
-  // producers sum h^2 over the CH lanes of a row.
+  // producers sum h^2 over the CH lanes of a row.  Each wave owns its strip, so
+  // only wave-level ordering is needed between the strip's LDS writes and
+  // reads: no block barrier, which would also wait for the strip's global
+  // stores to complete.
   float* strip = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
   const int mb = m0 + wm * TM * 16, nb = n0 + wn * TN * 16;
   constexpr int WC = TN * 16;                        // wave tile width
@@ -717,7 +725,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           strip[(ii * 16 + (lane >> 4) * 4 + e) * ELD + j * 16 + (lane & 15)] = acc[2 * i + ii][j][e];
-    __syncthreads();
+    wave_lds_fence();
     typename Epi::Pre8 pre[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
@@ -749,7 +757,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
         }
       }
     }
-    __syncthreads();
+    wave_lds_fence();
   }
 }
 

@@ -388,14 +388,14 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   a.ldo = h->qd;
   a.scale = 1.0f / std::sqrt((float)DH);
   const int nq = h->nh * h->S;
-  const int tiles = (nq + 127) / 128;
+  const int tiles = (nq + kAttnQueries - 1) / kAttnQueries;
   const int nblk = (L + KB - 1) / KB + (h->S + KB - 1) / KB;
   a.splits = attn_splits(B, tiles, nblk);
   a.tiles = tiles;
   a.partial = h->attn_partial;
   constexpr size_t smem = attn_smem_bytes<T, DH>();
   const int units = B * a.splits * tiles;
-  attn_kernel<T, DH><<<dim3(8 * ((units + 7) / 8)), dim3(512), smem, s>>>(a);
+  attn_kernel<T, DH><<<dim3(8 * ((units + 7) / 8)), dim3(AttnCfg<T>::NW * 64), smem, s>>>(a);
   PI0X_HIP(hipGetLastError());
   if (a.splits > 1) {
     attn_combine_kernel<T, DH><<<dim3(tiles, B, attn_combine_chunks<DH>()), dim3(512), 0, s>>>(a);
