@@ -185,6 +185,20 @@ def test_tiny_bf16_parity():
         c.ex.close()
 
 
+def test_tiny_bf16_batch8_tile_gemm_path():
+    # 8 x 9 = 72 suffix rows: the GEMMs take the tile kernel (more than 64 rows);
+    # the tiny q/k/v projection has 320 outputs, the 128x64 tile variant
+    w = TINY.replace(name="tiny_bf16_b8", dtype="bf16", batch=8, seed=11)
+    c = Case(w, norm_std=0.1)
+    try:
+        out = c.run()
+        ref = c.ref()
+        for b in range(w.batch):
+            check_close(out[b], ref[b], "bf16", f"tiny bf16 B=8 sample {b}")
+    finally:
+        c.ex.close()
+
+
 def test_call_argument_errors(tiny):
     from vla_flow_matching_amd import binding as b
     d = tiny.dev
@@ -213,6 +227,20 @@ def test_full_bf16_b1_parity():
     try:
         out = c.run()
         check_close(out, c.ref(), "bf16", "pi0 bf16 B=1 L=816 N=10")
+    finally:
+        c.ex.close()
+
+
+def test_full_bf16_b2_partial_row_tile_and_key_splits():
+    # 102 suffix rows (one partial 128-row GEMM tile); 2 x 4 query tiles, so the
+    # attention splits every sample's keys and merges the splits
+    w = synth.WORKLOADS["pi0_bf16_b1"].replace(name="pi0_bf16_b2", batch=2, num_steps=2, seed=3)
+    c = Case(w)
+    try:
+        out = c.run()
+        ref = c.ref()
+        for b in range(2):
+            check_close(out[b], ref[b], "bf16", f"pi0 bf16 B=2 N=2 sample {b}")
     finally:
         c.ex.close()
 

@@ -210,8 +210,13 @@ struct Timed {
 // ---------------------------------------------------------------------------
 // Column-group width of the sum-of-squares partials a residual producer writes
 // for M rows (the wave or block width of the kernel launch_gemm picks for it).
+// The bf16 path picks the batch-1 kernels when the call's suffix rows (B * S)
+// fit 64; every GEMM of the call then follows that choice, so the residual
+// producers of one call (suffix embedding, o_proj, down) write partials of one
+// group width.
+constexpr int kSmallRows = 64;
 int producer_group(bool bf16, int M) {
-  if (bf16) return M <= 64 ? kStreamGroup : 64;
+  if (bf16) return M <= kSmallRows ? kStreamGroup : 64;
   return M <= 1024 ? 32 : 64;
 }
 
@@ -260,11 +265,12 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi
   return PI0X_OK;
 }
 
-// Tile kernel configuration: 128x128 tiles, K slices of 64 double-buffered
-// (64 KB of LDS, 2 blocks per CU).
-template <int BK, int ST, class Epi>
-pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
-  constexpr int BM = 128, BN = 128;
+// Tile kernel configuration: 128x128 tiles (128x64 when N is not a multiple
+// of 128), K slices of 64 double-buffered (at most 64 KB of LDS, 2 blocks per
+// CU).
+template <int BN, class Epi>
+pi0x_status launch_gemm_tile_bn(hipStream_t s, GemmArgs g, const Epi& epi) {
+  constexpr int BM = 128, BK = 64, ST = 2;
   const int tm = (g.M + BM - 1) / BM, tn = g.N / BN;
   const int blocks = 8 * ((tm * tn + 7) / 8);
   constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST>();
@@ -275,7 +281,8 @@ pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
 
 template <class Epi>
 pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
-  return launch_gemm_tile_cfg<64, 2>(s, g, epi);
+  if (g.N % 128 == 0) return launch_gemm_tile_bn<128>(s, g, epi);
+  return launch_gemm_tile_bn<64>(s, g, epi);
 }
 
 template <int NW, int TN, class Epi>
@@ -310,12 +317,12 @@ pi0x_status launch_gemm_stream(pi0x_expert* h, hipStream_t s, GemmArgs g, const 
 // producer_group(); the other GEMMs pick their tiling for parallelism.
 template <typename T, class Epi>
 pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, const void* W, int M, int N, int K,
-                        const Epi& epi, NormIn nin = NormIn()) {
+                        const Epi& epi, NormIn nin = NormIn(), int path_rows = 0) {
   if (M <= 0) return PI0X_OK;
   if (K % 64 != 0 || N % 64 != 0) return fail(PI0X_ERR_SHAPE, "GEMM dims must be multiples of 64");
   const GemmArgs g = make_args(h, A, lda, W, M, N, K, nin);
   if constexpr (sizeof(T) == 2) {
-    if (M <= 64) {
+    if ((path_rows > 0 ? path_rows : M) <= kSmallRows) {
       // one kernel for the wide paired projection (gate/up): N alone fills the
       // chip, and a wave's K share fits its registers
       if constexpr (Epi::kPaired) {
@@ -326,8 +333,7 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
       }
       return launch_gemm_stream(h, s, g, epi);
     }
-    if (N % 128 == 0) return launch_gemm_tile(s, g, epi);
-    return fail(PI0X_ERR_SHAPE, "bf16 GEMM with more than 64 rows needs N % 128 == 0");
+    return launch_gemm_tile(s, g, epi);
   } else {
     if (M > 1024 && N % 128 == 0) return launch_gemm_cfg<T, 128, 128, 2, 2>(h, s, g, epi);
     if (M > 64) return launch_gemm_cfg<T, 128, 64, 2, 2>(h, s, g, epi);
@@ -340,6 +346,8 @@ template <class Epi>
 pi0x_status allow_tile_smem() {
   PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 128, 64, 2, 2, 2, Epi>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 64, 2>()));
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 64, 64, 2, 2, 2, Epi>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 64, 64, 2>()));
   return PI0X_OK;
 }
 
@@ -459,7 +467,6 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
   const void* hA = bf ? h->hb : (const void*)h->hbuf;
   // sum-of-squares partials: one per (row, producer column group)
   const int G = producer_group(bf, R);
-  if (producer_group(bf, AR) != G) return fail(PI0X_ERR_SHAPE, "inconsistent residual producer tiling");
   const int np = W / G;
   const NormIn nin{h->ssq, np};
 
@@ -499,7 +506,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
     PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, suffix_in());
     PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
                (launch_gemm<T>(h, s, h->u, W, h->w_mo, AR, W, W,
-                               EpiSuffixRows<T>{h->hbuf, hb, W, H, S, h->b_mo, h->ssq, np})));
+                               EpiSuffixRows<T>{h->hbuf, hb, W, H, S, h->b_mo, h->ssq, np}, NormIn(), R)));
     for (int l = 0; l < h->D; ++l) {
       const Layer& ly = h->layers[l];
       PI0X_TIMED(PI0X_KERNEL_QKV_ROPE,
