@@ -197,28 +197,35 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
     const int base = pre ? blk * KB : (blk - nb_pre) * KB;
     const int lim = pre ? valid : a.S;
 
-    // scores: lane holds query tile t's query (lane % 16) vs key kt*16 + 4g + e of the block
-    float sc[QT][KT][4];
+    // scores: lane holds query tile t's query (lane % 16) vs key kt*16 + 4g + e of
+    // the block.  The K-dimension loop is outermost so the KT x QT accumulator
+    // chains interleave; masking follows all the matrix-core work.
+    f32x4 acc[QT][KT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      f32x4 acc[QT];
+    for (int t = 0; t < QT; ++t)
 #pragma unroll
-      for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < KT; ++kt) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
         Frag<T> kf;
         load8(kf, &ks[(kt * 16 + (lane & 15)) * LDK + c * 32 + g * 8]);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t]);
+        for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t][kt]);
       }
+    float sc[QT][KT][4];
+    // suffix blocks: the state token (query s = 0) sees only key 0
+    const int state_lim = pre ? lim : 1;
 #pragma unroll
-      for (int t = 0; t < QT; ++t)
+    for (int t = 0; t < QT; ++t) {
+      const int tlim = qs[t] >= 1 ? lim : min(lim, state_lim);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = base + kt * 16 + g * 4 + e;
-          bool vis = key < lim;
-          if (!pre) vis = vis && (qs[t] >= 1 || key == 0);
-          sc[t][kt][e] = vis ? acc[t][e] * a.scale : -INFINITY;
+          sc[t][kt][e] = key < tlim ? acc[t][kt][e] * a.scale : -INFINITY;
         }
     }
     float m_new[QT];
