@@ -557,11 +557,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, Epi epi) {
 // tiles by all column tiles, so the blocks resident on one XCD share their A
 // row panels and W column panels in that XCD's L2.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int ST>
+template <int BM, int BN, int BK, int ST, int NWM = 2, int NWN = 2>
 constexpr size_t tile_smem_bytes() {
-  // the ring, or the epilogue strips of the 4 waves (32 rows x (BN/2 + 4) floats), whichever is larger
-  return (size_t)ST * (BM + BN) * BK * 2 > (size_t)4 * 32 * (BN / 2 + 4) * 4 ? (size_t)ST * (BM + BN) * BK * 2
-                                                                             : (size_t)4 * 32 * (BN / 2 + 4) * 4;
+  // the ring, or the epilogue strips of the waves (32 rows x (BN/NWN + 4) floats each), whichever is larger
+  return (size_t)ST * (BM + BN) * BK * 2 > (size_t)NWM * NWN * 32 * (BN / NWN + 4) * 4
+             ? (size_t)ST * (BM + BN) * BK * 2
+             : (size_t)NWM * NWN * 32 * (BN / NWN + 4) * 4;
 }
 
 __device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
   static_assert(BK == 32 || BK == 64, "slice width");
   static_assert(AJ >= 1 && BJ >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
   static_assert(TM % 2 == 0 && TN >= 1, "wave tile: 32-row strips of 16x16 tiles");
-  static_assert((size_t)(NT / 64) * 32 * ELD * 4 <= tile_smem_bytes<BM, BN, BK, ST>(), "epilogue staging must fit");
+  static_assert((size_t)(NT / 64) * 32 * ELD * 4 <= tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>(), "epilogue staging must fit");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* ring = reinterpret_cast<bf16*>(smem_raw);
   __shared__ float s_inv[BM];
