@@ -565,35 +565,6 @@ constexpr size_t tile_smem_bytes() {
              : (size_t)NWM * NWN * 32 * (BN / NWN + 4) * 4;
 }
 
-__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for
-// every outstanding global load (its fence covers the DMA writes), draining
-// the prefetch; the ring orders its DMA with explicit vmcnt waits instead, and
-// the empty asm statements only keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Orders one wave's LDS accesses across lanes: a wave's LDS instructions
-// execute in program order, so only the compiler has to be kept from moving
-// loads and stores across this point.
-__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
-
 // Waits until at most `ahead` ring stages of PER loads each are outstanding.
 template <int PER, int ST>
 __device__ __forceinline__ void wait_stages(int ahead) {
