@@ -199,6 +199,38 @@ def test_tiny_bf16_batch8_tile_gemm_path():
         c.ex.close()
 
 
+def test_tiny_fp32_batch8_split_k_path():
+    # 72 suffix rows in float32: the 128x64 float32 tiles with split K
+    w = TINY.replace(name="tiny_fp32_b8", batch=8, seed=13)
+    c = Case(w, norm_std=0.1)
+    try:
+        out = c.run()
+        check_close(out, c.ref(), "fp32", "tiny fp32 B=8")
+    finally:
+        c.ex.close()
+
+
+def test_tiny_bf16_zero_and_one_valid_prefix():
+    # valid lengths 0 and 1: an empty prefix (the state token attends to itself
+    # only) and a single key, through the bf16 batch-1-style kernels (18 rows)
+    w = TINY.replace(name="tiny_bf16_v01", dtype="bf16", batch=2, seed=17)
+    c = Case(w, norm_std=0.1)
+    try:
+        c.inputs["valid_len"][:] = [0, 1]
+        from vla_flow_matching_amd import binding
+        c.dev = binding.device_inputs(c.inputs, w.dtype)
+        out = c.run()
+        check_close(out, c.ref(), "bf16", "tiny bf16 valid 0 and 1")
+        kv = c.dev["prefix_kv"].clone()
+        kv[:, :, 0, 0:] = float("nan")
+        kv[:, :, 1, 1:] = float("nan")
+        d2 = dict(c.dev)
+        d2["prefix_kv"] = kv
+        assert np.array_equal(c.run(dev=d2), out), "padded prefix keys must never be read"
+    finally:
+        c.ex.close()
+
+
 def test_call_argument_errors(tiny):
     from vla_flow_matching_amd import binding as b
     d = tiny.dev
