@@ -353,14 +353,22 @@ struct EpiEuler {
   __device__ __forceinline__ void ssq(int, int, float) const {}
 };
 
-// inv_rms of rows m0 .. m0+n-1 into s_inv (threads < n), from the partials.
+// inv_rms of rows m0 .. m0+n-1 into s_inv (threads < n), from the partials
+// (16-byte loads, eight in flight, when the partial count is a multiple of 4).
 __device__ __forceinline__ void row_scale_prologue(const GemmArgs& g, int m0, int n, float* s_inv) {
   const int t = threadIdx.x;
   if (t < n) {
     float s = 0.f;
     if (m0 + t < g.M) {
       const float* p = g.ssq_in + (size_t)(m0 + t) * g.ssq_np;
-      for (int i = 0; i < g.ssq_np; ++i) s += p[i];
+      if (g.ssq_np % 4 == 0) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int i = 0; i < g.ssq_np; i += 4) acc += *reinterpret_cast<const f32x4*>(p + i);
+        s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      } else {
+        for (int i = 0; i < g.ssq_np; ++i) s += p[i];
+      }
     }
     s_inv[t] = 1.0f / sqrtf(s / (float)g.norm_dim + g.norm_eps);
   }

@@ -216,7 +216,7 @@ struct Timed {
 // group width.
 constexpr int kSmallRows = 64;
 int producer_group(bool bf16, int M) {
-  if (bf16) return M <= kSmallRows ? kStreamGroup : 64;
+  if (bf16) return M <= kSmallRows ? kStreamGroup : 32;  // tile kernel: 32-column wave tiles
   return M <= 1024 ? 32 : 64;
 }
 
@@ -265,12 +265,16 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi
   return PI0X_OK;
 }
 
-// Tile kernel configuration: 128x128 tiles (128x64 when N is not a multiple
-// of 128), K slices of 64 double-buffered (at most 64 KB of LDS, 2 blocks per
-// CU).
-template <int BN, class Epi>
-pi0x_status launch_gemm_tile_bn(hipStream_t s, GemmArgs g, const Epi& epi) {
-  constexpr int BM = 128, BK = 64, ST = 2;
+// Tile kernel configurations (128-row tiles, 2x2 waves, K slices of 64):
+// wide N (gate/up) takes 128x128 tiles double-buffered (64 KB of LDS, 2 blocks
+// per CU); the narrower projections take 128x64 tiles, so twice as many
+// blocks share the CUs -- double-buffered (48 KB, 3 blocks per CU) for
+// K <= 1024, three stages (72 KB, 2 blocks per CU) for the long-K o_proj and
+// down.  Residual producers (N = width) are always 128x64: their
+// sum-of-squares groups are the 32-column wave tiles.
+template <int BN, int ST, class Epi>
+pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
+  constexpr int BM = 128, BK = 64;
   const int tm = (g.M + BM - 1) / BM, tn = g.N / BN;
   const int blocks = 8 * ((tm * tn + 7) / 8);
   constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST>();
@@ -281,8 +285,9 @@ pi0x_status launch_gemm_tile_bn(hipStream_t s, GemmArgs g, const Epi& epi) {
 
 template <class Epi>
 pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
-  if (g.N % 128 == 0) return launch_gemm_tile_bn<128>(s, g, epi);
-  return launch_gemm_tile_bn<64>(s, g, epi);
+  if (g.N > 4096 && g.N % 128 == 0 && !Epi::kSsq) return launch_gemm_tile_cfg<128, 2>(s, g, epi);
+  if (g.K >= 2048) return launch_gemm_tile_cfg<64, 3>(s, g, epi);
+  return launch_gemm_tile_cfg<64, 2>(s, g, epi);
 }
 
 template <int NW, int TN, class Epi>
@@ -348,6 +353,8 @@ pi0x_status allow_tile_smem() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 128, 64, 2>()));
   PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 64, 64, 2, 2, 2, Epi>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 64, 64, 2>()));
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<128, 64, 64, 3, 2, 2, Epi>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<128, 64, 64, 3>()));
   return PI0X_OK;
 }
 
