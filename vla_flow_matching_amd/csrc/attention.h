@@ -59,11 +59,26 @@ template <> struct AttnCfg<bf16> { static constexpr int KB = 64, NW = 8, QT = 1;
 template <> struct AttnCfg<float> { static constexpr int KB = 32, NW = 8, QT = 1; };
 constexpr int kAttnQueries = 128;  // queries per block
 
+// LDS layout.  bf16 (head_dim a multiple of 64): unpadded 128-byte rows --
+// K split into head_dim/64 sub-tiles [KB][64], V^T [head_dim][KB = 64] -- with
+// the 16-byte chunks of row r at chunk ^ ((r / 2) % 8), so the fragment reads
+// (16 rows x 4 chunks per instruction) are free of bank conflicts.  float32
+// (and small head dims): rows padded by 16 bytes.
+template <typename T, int DH> struct AttnLds {
+  static constexpr bool kSwz = sizeof(T) == 2 && DH % 64 == 0 && AttnCfg<T>::KB == 64;
+  static constexpr int VE = 16 / (int)sizeof(T);
+  static constexpr int LDK = kSwz ? DH : DH + VE;  // K row (padded unless swizzled)
+  static constexpr int LDV = kSwz ? AttnCfg<T>::KB : AttnCfg<T>::KB + VE;
+};
+
 template <typename T, int DH>
 constexpr size_t attn_smem_bytes() {
-  constexpr int KB = AttnCfg<T>::KB, VE = 16 / (int)sizeof(T);
-  return (size_t)2 * (KB * (DH + VE) + DH * (KB + VE)) * sizeof(T);
+  constexpr int KB = AttnCfg<T>::KB;
+  return (size_t)2 * (KB * AttnLds<T, DH>::LDK + DH * AttnLds<T, DH>::LDV) * sizeof(T);
 }
+
+// element offset of 16-byte chunk ch (of 8 bf16) of swizzled row r (64 elements)
+__device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r >> 1) & 7)) << 3); }
 
 // exp for the softmax: the hardware exp2 path in bf16 mode, libm expf in float32 mode.
 template <typename T> __device__ __forceinline__ float fexp(float x) { return expf(x); }
@@ -76,8 +91,9 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int KT = KB / 16;   // 16-key score tiles per block
   constexpr int KS = KB / 32;   // 32-key PV steps per block
   constexpr int VE = 16 / (int)sizeof(T);
-  constexpr int LDK = DH + VE;  // padded K row
-  constexpr int LDV = KB + VE;  // padded V^T row
+  constexpr bool SWZ = AttnLds<T, DH>::kSwz;
+  constexpr int LDK = AttnLds<T, DH>::LDK;
+  constexpr int LDV = AttnLds<T, DH>::LDV;
   constexpr int NC = DH / 32, ND = DH / 16;
   constexpr int NVEC = KB * DH / VE;        // 16-byte vectors of K (and of V^T) per key block
   constexpr int KVEC = (NVEC + NT - 1) / NT;  // per thread
@@ -147,13 +163,15 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < KVEC; ++i) {
       const int v = tid + i * NT, kk = v / (DH / VE), dc = v % (DH / VE);
       if (!FULL && v >= NVEC) break;
-      *reinterpret_cast<u32x4*>(&ks[kk * LDK + dc * VE]) = ((kzero >> i) & 1u) ? u32x4{0u, 0u, 0u, 0u} : rk[i];
+      const int off = SWZ ? (dc >> 3) * (KB * 64) + swz64(kk, dc & 7) : kk * LDK + dc * VE;
+      *reinterpret_cast<u32x4*>(&ks[off]) = ((kzero >> i) & 1u) ? u32x4{0u, 0u, 0u, 0u} : rk[i];
     }
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
       const int v = tid + i * NT, d = v / (KB / VE), kc = (v % (KB / VE)) * VE;
       if (!FULL && v >= NVEC) break;
-      *reinterpret_cast<u32x4*>(&vt[d * LDV + kc]) = rv[i];
+      const int off = SWZ ? swz64(d, kc >> 3) : d * LDV + kc;
+      *reinterpret_cast<u32x4*>(&vt[off]) = rv[i];
     }
   };
 
@@ -210,7 +228,8 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         Frag<T> kf;
-        load8(kf, &ks[(kt * 16 + (lane & 15)) * LDK + c * 32 + g * 8]);
+        const int row = kt * 16 + (lane & 15);
+        load8(kf, &ks[SWZ ? (c >> 1) * (KB * 64) + swz64(row, (c & 1) * 4 + g) : row * LDK + c * 32 + g * 8]);
 #pragma unroll
         for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t][kt]);
       }
@@ -262,9 +281,10 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
         }
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
+        // keys 32 ks2 + {4g .. 4g+3, 16+4g .. 16+4g+3}: contiguous in the vt_pos order
         Frag<T> vf;
-        const T* vrow = &vt[(d * 16 + (lane & 15)) * LDV + ks2 * 32];
-        load4x2(vf, vrow + g * 4, vrow + 16 + g * 4);
+        const int row = d * 16 + (lane & 15);
+        load8(vf, &vt[SWZ ? swz64(row, ks2 * 4 + g) : row * LDV + ks2 * 32 + g * 8]);
 #pragma unroll
         for (int t = 0; t < QT; ++t) mma32(vf, pf[t], o[t][d]);
       }
@@ -343,8 +363,9 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
   for (int e = 0; e < 4; ++e) orow[d0 * 16 + g * 4 + e] = from_f32<T>(o[e] * inv);
 }
 
-// Prefix values, transposed once per call: vt[l][b][d][Lp] = V_l[b][key][d] for
-// keys < valid_len[b], 0 for the rest (padded keys are not read).  32 keys x 64
+// Prefix values, transposed once per call: vt[l][b][d][vt_pos(key)] =
+// V_l[b][key][d] for keys < valid_len[b], 0 for the rest (padded keys are not
+// read).  32 keys x 64
 // features per block through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const CallDesc* __restrict__ desc, int B, int L, int DH,
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const CallDesc* __rest
   T* dst = vt + ((size_t)lb * DH) * Lp;
   for (int i = threadIdx.x; i < 32 * 64; i += 256) {
     const int dd = i / 32, kk = i % 32;
-    if (d0 + dd < DH) dst[(size_t)(d0 + dd) * Lp + k0 + kk] = tileb[kk][dd];
+    if (d0 + dd < DH) dst[(size_t)(d0 + dd) * Lp + vt_pos(k0 + kk)] = tileb[kk][dd];
   }
 }
 

@@ -111,6 +111,14 @@ __device__ __forceinline__ void store8(bf16* p, const float* v) {
   *reinterpret_cast<bf16x8*>(p) = r;
 }
 
+// Key order of the transposed values (V^T) within every group of 32 keys:
+// key k = 16 h + 4 g + e (h < 2, g < 4, e < 4) is stored at 8 g + 4 h + e, so
+// the 8 keys one lane contributes to a 16x16x32 PV MFMA (4 g .. 4 g + 3 and
+// 16 + 4 g .. 16 + 4 g + 3) are contiguous: one 16-byte read.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l of the wave writes dst + 16 l bytes, dst wave-uniform.  Counted by
 // vmcnt like any other vector-memory load.

@@ -201,8 +201,8 @@ struct EpiResidual {
 // RoPE on every q head and the k head at position valid_len[b] + s for suffix
 // token s of sample b; the (cos, sin) pairs of every suffix row are tabulated
 // once per call in cs[row][head_dim/2].  q and k go to out[row][q heads | k] in
-// the natural layout; the values go transposed to vt[b][d][vt_ld] (column s),
-// the layout attention reads them in.
+// the natural layout; the values go transposed to vt[b][d][vt_ld] (column
+// vt_pos(s)), the layout attention reads them in.
 template <typename T>
 struct EpiQkvRope {
   static constexpr bool kPaired = true, kRowScale = true, kSsq = false;
@@ -230,7 +230,7 @@ struct EpiQkvRope {
       o[half] = from_f32<T>(x2 * cs_.x + x1 * cs_.y);
     } else {
       const int b = row / S, s = row - b * S;
-      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + s;
+      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + vt_pos(s);
       o[0] = from_f32<T>(x1);
       o[(size_t)16 * vt_ld] = from_f32<T>(x2);
     }
@@ -268,7 +268,7 @@ struct EpiQkvRope {
       store8(o + half, r2);
     } else {
       const int b = row / S, s = row - b * S;
-      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + s;
+      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + vt_pos(s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         o[(size_t)e * vt_ld] = from_f32<T>(x1[e]);
