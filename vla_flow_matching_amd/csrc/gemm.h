@@ -11,12 +11,13 @@
 //                     2x2 waves, K slices DMA'd straight into an LDS ring,
 //                     XCD-aware tile order: the compute-bound shapes (more
 //                     than 64 rows, i.e. batch >= 2).
-//  * gemm_wide_kernel  bf16, M <= 64, wide N (batch 1): one block per 16-32
-//                     columns over the whole K range, all loads in flight at
-//                     once, epilogue in the same kernel.
-//  * gemm_stream_kernel + gemm_reduce_kernel  bf16, M <= 64, narrow N or long
-//                     K (batch 1): split over N and K, the K-split partials
-//                     summed by the epilogue kernel.
+//  * gemm_wide_kernel  bf16, M <= 64 (batch 1), every projection but the
+//                     residual producers: one block per 16-32 columns over the
+//                     whole K range, a K chunk's loads in flight at once,
+//                     epilogue in the same kernel.
+//  * gemm_stream_kernel + gemm_reduce_kernel  bf16, M <= 64, the residual
+//                     producers (long K, N = width): split over N and K, the
+//                     K-split partials summed by the epilogue kernel.
 //
 // RMSNorm fusion.  The Gemma norm in front of the q/k/v and gate/up
 // projections is y = h / rms(h) * (1 + w); (1 + w) is folded into the weight
@@ -742,69 +743,76 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
 }
 
 // ---------------------------------------------------------------------------
-// gemm_wide_kernel: bf16, M <= 64 rows, BN = 16*TN output columns per block
-// and the whole K range, split evenly over NW waves (K / NW <= 256 elements
-// each).  Every wave issues all of its loads at once -- its weight rows and
-// its slice of all 64 activation rows (rows past M repeat row M-1) -- so one
-// memory round trip covers the block; the waves' tiles are then summed
-// through LDS and the epilogue runs in the same kernel.  Used where N alone
-// gives enough blocks to cover the chip.
+// gemm_wide_kernel: bf16, M <= 64 rows (batch 1), BN = 16*TN output columns
+// per block and the whole K range, split evenly over NW waves.  A wave takes
+// its K share in chunks of up to 256: it issues all loads of a chunk at once
+// -- its weight rows and its slice of the 64 activation rows (rows past M
+// repeat row M-1; their results are never stored) -- then runs the chunk's
+// MFMAs, so a chunk costs one memory round trip.  The waves' tiles are summed
+// through LDS and the epilogue runs in the same kernel: no K-split partials
+// and no second launch.  Every block reads the whole activation slice, so the
+// runtime keeps the long-K residual producers on the stream kernels; with
+// kSsq the kernel writes one sum-of-squares partial per (row, block), i.e.
+// per BN columns.
 // ---------------------------------------------------------------------------
 template <int NW, int TN, class Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_wide_kernel(GemmArgs g, Epi epi) {
   constexpr int NT = NW * 64, BN = TN * 16, LDR = BN + 1;
   constexpr int TPR = NT / 64;      // epilogue threads per row
   constexpr int CPT = BN / TPR;     // columns per thread in the epilogue
-  constexpr int KW = 256, NP = KW / 64;  // largest K share of a wave, in 64-wide chunks
+  constexpr int KW = 256, NP = KW / 64;  // K chunk of a wave, in 64-wide steps
   static_assert(!Epi::kPaired || (BN >= 32 && CPT % 2 == 0), "paired epilogues need 32-column groups");
-  static_assert(CPT >= 1, "too many threads for the tile");
+  static_assert(CPT >= 1 && (TPR & (TPR - 1)) == 0, "epilogue threads per row");
   __shared__ float red[NW][64 * LDR];
   __shared__ float s_inv[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN;
-  const int kw = g.K / NW, kb = wave * kw;  // this wave's K range [kb, kb + kw), kw % 64 == 0, kw <= KW
+  const int kw = g.K / NW, kb = wave * kw;  // this wave's K range [kb, kb + kw), kw % 64 == 0
   const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
 
   if constexpr (Epi::kRowScale) row_scale_prologue(g, 0, 64, s_inv);
 
   // lane (r, q) = (l % 16, l / 16): row/column r of each 16-tile, elements 16q .. 16q+15 of each
-  // 64-wide chunk (two MFMA steps of 8)
+  // 64-wide step (two MFMA steps of 8)
   const int fr = lane & 15, fk = (lane >> 4) * 16;
-  u32x4 wv[TN][NP][2], av[4][NP][2];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (p * 64 >= kw) break;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const bf16* src = W + (size_t)(n0 + j * 16 + fr) * g.ldw + kb + p * 64 + fk;
-      wv[j][p][0] = gload16(src);
-      wv[j][p][1] = gload16(src + 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16* src = A + (size_t)min(i * 16 + fr, g.M - 1) * g.lda + kb + p * 64 + fk;
-      av[i][p][0] = gload16(src);
-      av[i][p][1] = gload16(src + 8);
-    }
-  }
   f32x4 acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < kw; kc += KW) {
+    u32x4 wv[TN][NP][2], av[4][NP][2];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (p * 64 >= kw) break;
+    for (int p = 0; p < NP; ++p) {
+      if (kc + p * 64 >= kw) break;
+      const int k = kb + kc + p * 64 + fk;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int j = 0; j < TN; ++j) {
+        const bf16* src = W + (size_t)(n0 + j * 16 + fr) * g.ldw + k;
+        wv[j][p][0] = gload16(src);
+        wv[j][p][1] = gload16(src + 8);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const bf16* src = A + (size_t)min(i * 16 + fr, g.M - 1) * g.lda + k;
+        av[i][p][0] = gload16(src);
+        av[i][p][1] = gload16(src + 8);
+      }
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i][p][hh]),
-                                                              __builtin_bit_cast(bf16x8, wv[j][p][hh]), acc[i][j], 0, 0, 0);
+    for (int p = 0; p < NP; ++p) {
+      if (kc + p * 64 >= kw) break;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i][p][hh]),
+                                                                __builtin_bit_cast(bf16x8, wv[j][p][hh]), acc[i][j], 0, 0, 0);
+    }
   }
 
   // sum the waves' tiles
@@ -840,14 +848,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_wide_kernel(GemmArgs g, Epi epi)
       if (ok) epi.pair(row, n0 + c, tot(c), tot(c + 16), pre[e]);
     }
   } else {
-    static_assert(!Epi::kSsq, "residual producers use the stream kernels (256-column sum-of-squares groups)");
     typename Epi::Pre pre[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) pre[e] = epi.fetch(frow, n0 + q * CPT + e);
+    float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
       const int c = q * CPT + e;
-      if (ok) epi.one(row, n0 + c, tot(c), pre[e]);
+      if (ok) ss += epi.one(row, n0 + c, tot(c), pre[e]);
+    }
+    if constexpr (Epi::kSsq) {
+      // the TPR threads of a row are consecutive lanes of one wave
+#pragma unroll
+      for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      if (ok && q == 0) epi.ssq(row, blockIdx.x, ss);
     }
   }
 }

@@ -216,7 +216,7 @@ struct Timed {
 // group width.
 constexpr int kSmallRows = 64;
 int producer_group(bool bf16, int M) {
-  if (bf16) return M <= kSmallRows ? kStreamGroup : 32;  // tile kernel: 32-column wave tiles
+  if (bf16) return M <= kSmallRows ? kStreamGroup : 32;  // stream reduce waves / tile kernel's 32-column wave tiles
   return M <= 1024 ? 32 : 64;
 }
 
@@ -328,15 +328,18 @@ pi0x_status launch_gemm(pi0x_expert* h, hipStream_t s, const void* A, int lda, c
   const GemmArgs g = make_args(h, A, lda, W, M, N, K, nin);
   if constexpr (sizeof(T) == 2) {
     if ((path_rows > 0 ? path_rows : M) <= kSmallRows) {
-      // one kernel for the wide paired projection (gate/up): N alone fills the
-      // chip, and a wave's K share fits its registers
-      if constexpr (Epi::kPaired) {
-        if (N % 32 == 0 && N / 32 >= 128) {
-          if (K <= 2048 && K % 512 == 0) return launch_gemm_wide<8, 2>(s, g, epi);
-          if (K <= 1024 && K % 256 == 0) return launch_gemm_wide<4, 2>(s, g, epi);
-        }
+      // Residual producers (the long-K o_proj and down, N = width) split K
+      // over blocks: every wide block would read the whole activation slice.
+      // The others run one kernel over the whole K: blocks of 16 (32 for
+      // paired epilogues) columns, K split over 8 waves where K allows.
+      if constexpr (Epi::kSsq) {
+        return launch_gemm_stream(h, s, g, epi);
+      } else {
+        constexpr int TN = Epi::kPaired ? 2 : 1;
+        if (K % 512 == 0) return launch_gemm_wide<8, TN>(s, g, epi);
+        if (K % 256 == 0) return launch_gemm_wide<4, TN>(s, g, epi);
+        return launch_gemm_wide<1, TN>(s, g, epi);
       }
-      return launch_gemm_stream(h, s, g, epi);
     }
     return launch_gemm_tile(s, g, epi);
   } else {
