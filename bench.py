@@ -102,7 +102,7 @@ def measured_traffic(workload: str, kernel: str):
     return float(e["bytes_per_launch"])
 
 
-def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
+def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2, latency_calls: int = 100):
     import torch
     from vla_flow_matching_amd import binding, synth
 
@@ -132,6 +132,18 @@ def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     assert np.all(np.isfinite(out.cpu().numpy())), "non-finite actions"
+
+    # per-launch latency distribution: each call bracketed by its own events
+    lat = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(latency_calls)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: float(np.percentile(lat, q)) if lat else None
+    dist = {"median_ms": pct(50), "p10_ms": pct(10), "p90_ms": pct(90), "launches": len(lat)}
 
     # per-kernel durations: the same loop launched eagerly with HIP events
     ex.set_timing(True)
@@ -168,7 +180,7 @@ def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2):
              "mfma_frac": counts["flops"] / sec / 1e12 / (MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS),
              "bytes_per_call": counts["bytes"], "flops_per_call": counts["flops"]}
     return {"workload": w, "ms": ms, "value": w.batch / sec, "roofline": roof, "kernels": kern, "whole_loop": whole,
-            "inputs": inputs}
+            "latency": dist, "inputs": inputs}
 
 
 def cpu_baseline(w, inputs, budget_s: float = 12.0):
@@ -204,6 +216,8 @@ def main():
     ap.add_argument("--workload", default="pi0_bf16_b64")
     ap.add_argument("--b1-workload", default="pi0_bf16_b1", help="secondary latency workload ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--latency-calls", type=int, default=100,
+                    help="calls timed one by one for the latency median / p10 / p90 (0 to skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size reference "
                          "kernel for HBM byte counters)")
@@ -222,7 +236,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    main_res = run_workload(args.workload, args.steps, args.warmup)
+    main_res = run_workload(args.workload, args.steps, args.warmup, latency_calls=args.latency_calls)
     w = main_res["workload"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
@@ -233,11 +247,13 @@ def main():
         "roofline": main_res["roofline"],
         "whole_loop": main_res["whole_loop"],
         "kernels": main_res["kernels"],
+        "latency": main_res["latency"],
     }
     if args.b1_workload:
-        r = run_workload(args.b1_workload, max(args.steps, 20), args.warmup)
+        r = run_workload(args.b1_workload, max(args.steps, 20), args.warmup, latency_calls=args.latency_calls)
         line["b1"] = {"workload": r["workload"].name, "chunks_per_s": r["value"], "latency_ms": r["ms"],
-                      "roofline": r["roofline"], "whole_loop": r["whole_loop"], "kernels": r["kernels"]}
+                      "latency": r["latency"], "roofline": r["roofline"], "whole_loop": r["whole_loop"],
+                      "kernels": r["kernels"]}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, main_res["inputs"])
     print(json.dumps(line), flush=True)
