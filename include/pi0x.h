@@ -137,6 +137,36 @@ pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len,
                               const int32_t* prefix_valid_len, const float* state, const float* x_t, float t,
                               float* v_out, hipStream_t stream);
 
+/*
+ * Boundary normalization (page 1, _build_norm_buffers and _apply_norm: the
+ * LeRobot NormalizationMode semantics).  Statistics cover the first `count`
+ * features; the remaining ones pass through unchanged.
+ *   MEAN_STD  a = mean, b = std.  Forward (state):   (x - mean) / (std + 1e-8).
+ *                                 Inverse (actions): x * std + mean.
+ *   MIN_MAX   a = min,  b = max,  d = max(max - min, 1e-8).
+ *                                 Forward (state):   2 (x - min) / d - 1.
+ *                                 Inverse (actions): (x + 1) / 2 * d + min.
+ * All arithmetic is float32.
+ */
+typedef enum { PI0X_NORM_NONE = 0, PI0X_NORM_MEAN_STD = 1, PI0X_NORM_MIN_MAX = 2 } pi0x_norm_mode;
+typedef struct {
+  int32_t mode;    /* pi0x_norm_mode */
+  int32_t count;   /* features covered: 1 .. state_dim (state) or 1 .. action_dim (actions) */
+  const float* a;  /* host float32 [count]: mean or min */
+  const float* b;  /* host float32 [count]: std or max */
+} pi0x_norm;
+
+/* Sets the normalization of later calls on the handle; the statistics are
+ * copied.  state: the proprioceptive state is normalized before state_proj
+ * (pi0x_denoise and pi0x_denoise_step).  action: the action chunk returned by
+ * pi0x_denoise is unnormalized; the loop itself runs in the normalized space
+ * and pi0x_denoise_step returns the raw velocity.  NULL or PI0X_NORM_NONE
+ * turns a side off (the state at creation).  Synchronous: the caller must
+ * have synchronised every stream with calls in flight on the handle.
+ * Errors: PI0X_ERR_INVALID_ARG for a NULL handle, an unknown mode, a count
+ * outside the range above or NULL statistics; nothing changes then. */
+pi0x_status pi0x_set_normalization(pi0x_expert* h, const pi0x_norm* state, const pi0x_norm* action);
+
 /* Releases the handle and everything it owns (synchronises the device first).
  * NULL is ignored. */
 void pi0x_expert_destroy(pi0x_expert* h);

@@ -68,6 +68,8 @@ def _load():
                                      ctypes.c_double, _D]
         lib.pi0o_step_time.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.pi0o_step_time.restype = ctypes.c_double
+        lib.pi0o_apply_norm.argtypes = [_D, ctypes.c_int, ctypes.c_int, _D, _D, ctypes.c_int, ctypes.c_int]
+        lib.pi0o_apply_norm.restype = None
         _lib = lib
     return _lib
 
@@ -114,6 +116,31 @@ def silu(x: float) -> float:
 
 def step_time(k: int, num_steps: int) -> float:
     return _load().pi0o_step_time(int(k), int(num_steps))
+
+
+def apply_norm(x, stats: dict | None, inverse: bool) -> np.ndarray:
+    """Boundary (un)normalization of the last axis (page 1, _apply_norm) in
+    fp64; stats in the page's format ({"mode": "mean_std", "mean", "std"} or
+    {"mode": "min_max", "min", "max"}), None: unchanged.  The statistics go
+    through float32 first, as the boundary takes them."""
+    x = _f64(x).copy()
+    if not stats:
+        return x
+    mode = str(stats.get("mode", "mean_std")).lower()
+    if mode == "mean_std":
+        a, b, m = stats["mean"], stats["std"], 1
+    elif mode == "min_max":
+        a, b, m = stats["min"], stats["max"], 2
+    else:
+        raise ValueError(mode)
+    a = _f64(np.asarray(a, dtype=np.float32))
+    b = _f64(np.asarray(b, dtype=np.float32))
+    rows = x.reshape(-1, x.shape[-1])
+    for r in range(rows.shape[0]):
+        row = np.ascontiguousarray(rows[r])
+        _load().pi0o_apply_norm(_p(row), row.size, m, _p(a), _p(b), a.size, int(bool(inverse)))
+        rows[r] = row
+    return rows.reshape(x.shape)
 
 
 def attend_one(q, kp, vp, valid: int, ks, vs, r: int, scale: float) -> np.ndarray:
@@ -198,13 +225,17 @@ class Oracle:
                              int(L), int(valid), int(num_steps), float(pos_shift), _p(out))
         return out
 
-    def denoise_batch(self, inputs: dict, num_steps: int, samples=None) -> np.ndarray:
-        """Run samples (default: all) of a batch laid out as the boundary takes it."""
+    def denoise_batch(self, inputs: dict, num_steps: int, samples=None, state_norm: dict | None = None,
+                      action_norm: dict | None = None) -> np.ndarray:
+        """Run samples (default: all) of a batch laid out as the boundary takes it.
+        state_norm / action_norm: the state is normalized before the loop and the
+        returned actions unnormalized (page 1, _normalize_state / _unnormalize_actions)."""
         kv = inputs["prefix_kv"]
         B, L = kv.shape[2], kv.shape[3]
         idx = range(B) if samples is None else samples
         outs = []
         for b in idx:
-            outs.append(self.denoise(inputs["state"][b], inputs["noise"][b], kv[:, :, b], L,
-                                     int(inputs["valid_len"][b]), num_steps))
+            state = apply_norm(inputs["state"][b], state_norm, inverse=False)
+            x = self.denoise(state, inputs["noise"][b], kv[:, :, b], L, int(inputs["valid_len"][b]), num_steps)
+            outs.append(apply_norm(x, action_norm, inverse=True))
         return np.stack(outs)

@@ -342,6 +342,25 @@ void pi0o_denoise(const pi0o_cfg* c, const double* w, const double* state, const
   free(v);
 }
 
+/* Boundary normalization (page 1, _build_norm_buffers and _apply_norm), in
+ * place on x[n]: mode 1 mean/std (a = mean, b = std), mode 2 min/max (a = min,
+ * b = max).  Only features j < count change.  Forward (the state):
+ * mean/std (x - mean) / (std + 1e-8); min/max 2 (x - min) / d - 1 with
+ * d = max(max - min, 1e-8).  Inverse (the actions): mean/std x std + mean;
+ * min/max (x + 1) / 2 * d + min. */
+void pi0o_apply_norm(double* x, int n, int mode, const double* a, const double* b, int count, int inverse) {
+  const double eps = 1e-8;
+  for (int j = 0; j < n && j < count; ++j) {
+    if (mode == 1) {
+      x[j] = inverse ? x[j] * b[j] + a[j] : (x[j] - a[j]) / (b[j] + eps);
+    } else if (mode == 2) {
+      double d = b[j] - a[j];
+      if (d < eps) d = eps;
+      x[j] = inverse ? (x[j] + 1.0) * 0.5 * d + a[j] : 2.0 * (x[j] - a[j]) / d - 1.0;
+    }
+  }
+}
+
 /* Time value the sampler evaluates at step k of N (exposed for tests). */
 double pi0o_step_time(int k, int num_steps) {
   double dt = -1.0 / (double)num_steps;

@@ -16,7 +16,7 @@ def test_library_exports_every_declared_function():
     names = b.declared_functions()
     assert set(names) == {"pi0x_config_default", "pi0x_weight_count", "pi0x_expert_create", "pi0x_denoise",
                           "pi0x_denoise_step", "pi0x_expert_destroy", "pi0x_last_error", "pi0x_set_timing",
-                          "pi0x_read_timing"}
+                          "pi0x_read_timing", "pi0x_set_normalization"}
     lib = b.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -86,3 +86,7 @@ def test_calls_reject_null_handle():
     assert b.pi0x_set_timing(None, 1) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_read_timing(None)[0] == b.PI0X_ERR_INVALID_ARG
     b.pi0x_expert_destroy(None)  # ignored
+
+
+def test_set_normalization_null_handle():
+    assert b.lib().pi0x_set_normalization(None, None, None) == b.PI0X_ERR_INVALID_ARG

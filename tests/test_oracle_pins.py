@@ -415,3 +415,58 @@ def test_oracle_matches_page_formulation_gqa_two_kv_heads():
     ref = PageFormulation(s, blob).denoise(inp, 2)
     ours = oracle.Oracle(s, blob).denoise_batch(inp, 2)
     assert np.max(np.abs(ours - ref)) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# Boundary normalization (page 1, _build_norm_buffers / _apply_norm)
+# ---------------------------------------------------------------------------
+
+def test_norm_min_max_maps_range_onto_unit_interval_and_back():
+    # the page: forward maps [min, max] into [-1, 1], inverse maps back
+    lo = np.array([-2.0, 0.5, 3.0], np.float32)
+    hi = np.array([2.0, 1.5, 7.0], np.float32)
+    st = {"mode": "min_max", "min": lo, "max": hi}
+    x = np.stack([lo, hi, (lo.astype(np.float64) + hi) / 2])
+    y = oracle.apply_norm(x, st, inverse=False)
+    assert np.allclose(y[0], -1.0, atol=1e-15) and np.allclose(y[1], 1.0, atol=1e-15)
+    assert np.allclose(y[2], 0.0, atol=1e-15)
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((5, 3))
+    assert np.allclose(oracle.apply_norm(oracle.apply_norm(z, st, False), st, True), z, atol=1e-12)
+    assert np.allclose(oracle.apply_norm(oracle.apply_norm(z, st, True), st, False), z, atol=1e-12)
+
+
+def test_norm_min_max_degenerate_range_clamps_denominator():
+    # max == min: the denominator is clamped at 1e-8
+    st = {"mode": "min_max", "min": np.array([1.0], np.float32), "max": np.array([1.0], np.float32)}
+    y = oracle.apply_norm(np.array([1.0, 1.0 + 1e-8]), st, False)
+    assert y[0] == -1.0 and abs(y[1] - 1.0) < 1e-7
+    assert oracle.apply_norm(np.array([1.0]), st, True)[0] == 1.0 + 1e-8
+
+
+def test_norm_mean_std_closed_forms():
+    mean = np.array([0.5, -1.0], np.float32)
+    std = np.array([2.0, 0.25], np.float32)
+    st = {"mode": "mean_std", "mean": mean, "std": std}
+    m, s = mean.astype(np.float64), std.astype(np.float64)
+    assert np.allclose(oracle.apply_norm(m, st, False), 0.0, atol=1e-15)
+    assert np.allclose(oracle.apply_norm(m + s, st, False), s / (s + 1e-8), atol=1e-15)
+    assert np.allclose(oracle.apply_norm(np.zeros(2), st, True), m, atol=1e-15)
+    assert np.allclose(oracle.apply_norm(np.ones(2), st, True), m + s, atol=1e-15)
+    # forward divides by std + 1e-8, inverse multiplies by std: the round trip
+    # shrinks x - mean by std / (std + 1e-8)
+    x = np.array([3.0, 7.0])
+    rt = oracle.apply_norm(oracle.apply_norm(x, st, False), st, True)
+    assert np.allclose(rt, m + (x - m) * s / (s + 1e-8), atol=1e-12)
+
+
+def test_norm_touches_only_the_leading_features_and_none_is_identity():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 6))
+    for st in ({"mode": "mean_std", "mean": [1.0, 2.0], "std": [3.0, 4.0]},
+               {"mode": "min_max", "min": [-1.0, -2.0], "max": [1.0, 2.0]}):
+        for inv in (False, True):
+            y = oracle.apply_norm(x, st, inv)
+            assert np.array_equal(y[:, 2:], x[:, 2:])
+            assert not np.allclose(y[:, :2], x[:, :2])
+    assert np.array_equal(oracle.apply_norm(x, None, False), x)

@@ -36,6 +36,16 @@ class pi0x_config(ctypes.Structure):
         [("dtype", ctypes.c_int32), ("use_graphs", ctypes.c_int32)]
 
 
+PI0X_NORM_NONE = 0
+PI0X_NORM_MEAN_STD = 1
+PI0X_NORM_MIN_MAX = 2
+
+
+class pi0x_norm(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("a", ctypes.POINTER(ctypes.c_float)), ("b", ctypes.POINTER(ctypes.c_float))]
+
+
 class Pi0xError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"pi0x status {status}: {msg}")
@@ -74,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.pi0x_expert_destroy.restype = None
         L.pi0x_last_error.argtypes = []
         L.pi0x_last_error.restype = ctypes.c_char_p
+        L.pi0x_set_normalization.restype = i32
+        L.pi0x_set_normalization.argtypes = [vp, ctypes.POINTER(pi0x_norm), ctypes.POINTER(pi0x_norm)]
         L.pi0x_set_timing.argtypes = [vp, i32]
         L.pi0x_set_timing.restype = i32
         L.pi0x_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -116,6 +128,32 @@ def pi0x_expert_destroy(h) -> None:
 
 
 KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final"]
+
+
+def norm_struct(stats: dict | None):
+    """pi0x_norm for {"mode": "mean_std", "mean": [...], "std": [...]} or
+    {"mode": "min_max", "min": [...], "max": [...]} (None: off).  Returns the
+    struct and the float32 arrays it points into (keep them alive for the call)."""
+    if not stats:
+        return None, ()
+    mode = str(stats.get("mode", "mean_std")).lower()
+    if mode == "mean_std":
+        a, b, m = stats["mean"], stats["std"], PI0X_NORM_MEAN_STD
+    elif mode == "min_max":
+        a, b, m = stats["min"], stats["max"], PI0X_NORM_MIN_MAX
+    else:
+        raise ValueError(f"unknown normalization mode {mode!r}")
+    a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    b = np.ascontiguousarray(b, dtype=np.float32).ravel()
+    fp = ctypes.POINTER(ctypes.c_float)
+    return pi0x_norm(m, a.size, a.ctypes.data_as(fp), b.ctypes.data_as(fp)), (a, b)
+
+
+def pi0x_set_normalization(h, state: dict | None, action: dict | None) -> int:
+    ns, keep_s = norm_struct(state)
+    na, keep_a = norm_struct(action)
+    return lib().pi0x_set_normalization(h, ctypes.byref(ns) if ns is not None else None,
+                                        ctypes.byref(na) if na is not None else None)
 
 
 def pi0x_set_timing(h, enable: bool) -> int:
@@ -186,6 +224,10 @@ class Expert:
         check(pi0x_denoise_step(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                                 self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
         return out
+
+    def set_normalization(self, state: dict | None = None, action: dict | None = None):
+        """State / action statistics in the page's format (see norm_struct); None turns a side off."""
+        check(pi0x_set_normalization(self.h, state, action))
 
     def set_timing(self, enable: bool):
         check(pi0x_set_timing(self.h, enable))

@@ -24,6 +24,32 @@ struct CallDesc {
   float t;               // single step: the time value
 };
 
+// Boundary normalization statistics (page 1, _build_norm_buffers /
+// _apply_norm), set by pi0x_set_normalization and read by the kernels on
+// every call.  mode 0: none; 1: mean/std; 2: min/max.  Only the first count
+// features are transformed; the rest pass through.  Host-prepared float32:
+//   state  (forward):  mean/std  (s - a) / d         with d = std + 1e-8
+//                      min/max   2 (s - a) / d - 1   with d = max(max - min, 1e-8)
+//   action (inverse):  mean/std  x d + a             with d = std
+//                      min/max   (x + 1) / 2 d + a   with d = max(max - min, 1e-8)
+constexpr int kNormMaxDim = 64;
+struct NormDev {
+  int state_mode, state_count, action_mode, action_count;
+  float sa[kNormMaxDim], sd[kNormMaxDim];
+  float aa[kNormMaxDim], ad[kNormMaxDim];
+};
+
+__device__ __forceinline__ float norm_state(const NormDev* n, int j, float x) {
+  if (n->state_mode == 0 || j >= n->state_count) return x;
+  if (n->state_mode == 1) return (x - n->sa[j]) / n->sd[j];
+  return 2.0f * (x - n->sa[j]) / n->sd[j] - 1.0f;
+}
+__device__ __forceinline__ float unnorm_action(const NormDev* n, int j, float x) {
+  if (n->action_mode == 0 || j >= n->action_count) return x;
+  if (n->action_mode == 1) return x * n->ad[j] + n->aa[j];
+  return (x + 1.0f) * 0.5f * n->ad[j] + n->aa[j];
+}
+
 // 16-byte load through a global-address-space pointer.  Pointers read from
 // memory (the call descriptor) are generic to the compiler; generic loads
 // also count against the LDS counter, so a later LDS wait would stall on them.

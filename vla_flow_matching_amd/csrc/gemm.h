@@ -306,7 +306,8 @@ struct EpiGeglu {
 // norm: GEMM row r is hidden row r of the suffix, column c < A an action
 // feature.  The state rows (r % S == 0) and padding columns are dropped.
 // v = acc + b_out[c]; mode 0: x <- x + dt v (x from desc->x_in on the first
-// step, else x_loop; written to x_loop and, on the last step, to desc->out);
+// step, else x_loop; written to x_loop and, on the last step, to desc->out
+// after the action unnormalization, page 1 _apply_norm inverse, when set);
 // mode 1: v is written to desc->out.
 struct EpiEuler {
   static constexpr bool kPaired = false, kRowScale = true, kSsq = false;
@@ -317,6 +318,7 @@ struct EpiEuler {
   int H, S, A;
   int from_input, write_out, mode;
   float dt;
+  const NormDev* norm;  // action unnormalization of the returned chunk (write_out)
   __device__ __forceinline__ int idx(int row, int col) const {
     const int b = row / S, s = row - b * S;
     return (s == 0 || col >= A) ? -1 : (b * H + s - 1) * A + col;
@@ -335,7 +337,7 @@ struct EpiEuler {
     } else {
       const float xn = x + dt * v;
       x_loop[i] = xn;
-      if (write_out) desc->out[i] = xn;
+      if (write_out) desc->out[i] = unnorm_action(norm, col, xn);
     }
     return 0.f;
   }

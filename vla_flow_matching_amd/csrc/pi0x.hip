@@ -126,6 +126,7 @@ struct pi0x_expert {
   float* attn_partial = nullptr;  // split attention states [blocks][2 + head_dim/4][512]
   unsigned* gemm_counters = nullptr;
   CallDesc* desc = nullptr;
+  NormDev* norm = nullptr;  // boundary normalization statistics (all modes 0 at create)
   hipStream_t cap_stream = nullptr;
   std::map<Key, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
   std::vector<Key> graph_order;
@@ -492,7 +493,8 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
              (launch_gemm<T>(h, s, h->tau, W, h->w_tt, steps, W, W, EpiStore<float>{h->tbias, W, h->b_mi, 0})));
   PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_transpose_v<T>(h, s, B, L));
   auto state_tok = [&]() -> pi0x_status {
-    hipLaunchKernelGGL(state_token_kernel, dim3(B), dim3(256), 0, s, h->desc, h->Sd, W, h->w_s, h->b_s, h->hs);
+    hipLaunchKernelGGL(state_token_kernel, dim3(B), dim3(256), 0, s, h->desc, h->norm, h->Sd, W, h->w_s, h->b_s,
+                       h->hs);
     PI0X_HIP(hipGetLastError());
     return PI0X_OK;
   };
@@ -535,7 +537,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
     const int last = (k == steps - 1);
     PI0X_TIMED(PI0X_KERNEL_FINAL,
                (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W,
-                               EpiEuler{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1, dt}, nin)));
+                               EpiEuler{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1, dt, h->norm}, nin)));
   }
   return PI0X_OK;
 }
@@ -800,6 +802,11 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
     PI0X_HIP(hipMemset(h->gemm_counters, 0, (size_t)kCounters * 4));
   }
   PI0X_TRY(h->allocT(&h->desc, sizeof(CallDesc)));
+  PI0X_TRY(h->allocT(&h->norm, sizeof(NormDev)));
+  {
+    const NormDev none{};
+    PI0X_HIP(hipMemcpy(h->norm, &none, sizeof(NormDev), hipMemcpyHostToDevice));
+  }
   PI0X_HIP(hipMemset(h->desc, 0, sizeof(CallDesc)));
   const int P = h->Lmax + h->S + 1;
   PI0X_TRY(h->allocT(&h->rope_cos, (size_t)P * (h->dh / 2) * 4));
@@ -923,6 +930,40 @@ pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len,
                      v_out, t);
   PI0X_HIP(hipGetLastError());
   return run(h, batch, prefix_len, 0, stream);
+}
+
+pi0x_status pi0x_set_normalization(pi0x_expert* h, const pi0x_norm* state, const pi0x_norm* action) {
+  if (!h) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  NormDev n{};
+  auto fill = [](const pi0x_norm* in, int dim, bool forward, int* mode, int* count, float* a, float* d,
+                 const char* what) -> pi0x_status {
+    *mode = 0;
+    *count = 0;
+    if (!in || in->mode == PI0X_NORM_NONE) return PI0X_OK;
+    if (in->mode != PI0X_NORM_MEAN_STD && in->mode != PI0X_NORM_MIN_MAX)
+      return fail(PI0X_ERR_INVALID_ARG, std::string(what) + " normalization: unknown mode");
+    if (in->count < 1 || in->count > dim)
+      return fail(PI0X_ERR_INVALID_ARG, std::string(what) + " normalization: count must be in [1, " +
+                                            std::to_string(dim) + "]");
+    if (!in->a || !in->b) return fail(PI0X_ERR_INVALID_ARG, std::string(what) + " normalization: NULL statistics");
+    *mode = in->mode;
+    *count = in->count;
+    for (int j = 0; j < in->count; ++j) {
+      a[j] = in->a[j];
+      if (in->mode == PI0X_NORM_MEAN_STD) d[j] = forward ? in->b[j] + 1e-8f : in->b[j];
+      else d[j] = std::max(in->b[j] - in->a[j], 1e-8f);
+    }
+    return PI0X_OK;
+  };
+  PI0X_TRY(fill(state, h->Sd, true, &n.state_mode, &n.state_count, n.sa, n.sd, "state"));
+  PI0X_TRY(fill(action, h->A, false, &n.action_mode, &n.action_count, n.aa, n.ad, "action"));
+  int cur = 0;
+  PI0X_HIP(hipGetDevice(&cur));
+  PI0X_HIP(hipSetDevice(h->device));
+  const hipError_t e = hipMemcpy(h->norm, &n, sizeof(NormDev), hipMemcpyHostToDevice);
+  (void)hipSetDevice(cur);
+  PI0X_HIP(e);
+  return PI0X_OK;
 }
 
 void pi0x_expert_destroy(pi0x_expert* h) {

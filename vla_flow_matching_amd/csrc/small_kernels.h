@@ -20,12 +20,12 @@ __global__ void set_desc_kernel(CallDesc* d, const void* kv, const int32_t* vali
 // State token of every sample (page 1, embed_suffix: state_proj(state)),
 // once per call: hs[b][o] = W_s s_b + b_s (float32).  The token depends on
 // neither x nor t.  One block per sample.
-__global__ __launch_bounds__(256) void state_token_kernel(const CallDesc* __restrict__ desc, int Sd, int W,
-                                                          const float* __restrict__ w_s, const float* __restrict__ b_s,
-                                                          float* __restrict__ hs) {
+__global__ __launch_bounds__(256) void state_token_kernel(const CallDesc* __restrict__ desc, const NormDev* __restrict__ norm,
+                                                          int Sd, int W, const float* __restrict__ w_s,
+                                                          const float* __restrict__ b_s, float* __restrict__ hs) {
   __shared__ float xs[64];
   const int b = blockIdx.x;
-  if (threadIdx.x < Sd) xs[threadIdx.x] = desc->state[(size_t)b * Sd + threadIdx.x];
+  if (threadIdx.x < Sd) xs[threadIdx.x] = norm_state(norm, threadIdx.x, desc->state[(size_t)b * Sd + threadIdx.x]);
   __syncthreads();
   for (int o = threadIdx.x; o < W; o += 256) {
     const float* wr = w_s + (size_t)o * Sd;
