@@ -58,14 +58,19 @@ def _load():
         lib.pi0o_silu.argtypes = [ctypes.c_double]
         lib.pi0o_silu.restype = ctypes.c_double
         lib.pi0o_attend_one.argtypes = [_D, ctypes.c_int, ctypes.c_double, _D, _D, ctypes.c_int, _D, _D,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_size_t, _D]
-        lib.pi0o_expert_layer.argtypes = [P, _D, _D, ctypes.c_int, _D, _D, ctypes.c_int, _D]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, _D]
+        lib.pi0o_expert_layer.argtypes = [P, _D, _D, ctypes.c_int, _D, _D, ctypes.c_int, _D, ctypes.c_int]
         lib.pi0o_embed_suffix.argtypes = [P, _D, _D, _D, ctypes.c_double, _D]
-        lib.pi0o_expert_forward.argtypes = [P, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.pi0o_expert_forward.argtypes = [P, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                            ctypes.c_int]
         lib.pi0o_velocity.argtypes = [P, _D, _D, _D, ctypes.c_double, _D, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_double, _D]
+                                      ctypes.c_double, ctypes.c_int, _D]
         lib.pi0o_denoise.argtypes = [P, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_double, _D]
+        lib.pi0o_denoise_ex.argtypes = [P, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D, _D]
+        lib.pi0o_step_schedule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D]
+        lib.pi0o_step_schedule.restype = None
         lib.pi0o_step_time.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.pi0o_step_time.restype = ctypes.c_double
         lib.pi0o_apply_norm.argtypes = [_D, ctypes.c_int, ctypes.c_int, _D, _D, ctypes.c_int, ctypes.c_int]
@@ -118,6 +123,17 @@ def step_time(k: int, num_steps: int) -> float:
     return _load().pi0o_step_time(int(k), int(num_steps))
 
 
+SCHEDULES = {"pi0": 0, "zero_to_one": 1}
+
+
+def step_schedule(k: int, num_steps: int, schedule: str = "pi0") -> tuple[float, float]:
+    """(t_k, dt_k) of step k: "pi0" runs t from 1 down (dt = -1/N), "zero_to_one"
+    the float32 grid k/N from 0 up (dt_k = t_{k+1} - t_k)."""
+    t, dt = ctypes.c_double(), ctypes.c_double()
+    _load().pi0o_step_schedule(int(k), int(num_steps), SCHEDULES[schedule], ctypes.byref(t), ctypes.byref(dt))
+    return t.value, dt.value
+
+
 def apply_norm(x, stats: dict | None, inverse: bool) -> np.ndarray:
     """Boundary (un)normalization of the last axis (page 1, _apply_norm) in
     fp64; stats in the page's format ({"mode": "mean_std", "mean", "std"} or
@@ -143,14 +159,14 @@ def apply_norm(x, stats: dict | None, inverse: bool) -> np.ndarray:
     return rows.reshape(x.shape)
 
 
-def attend_one(q, kp, vp, valid: int, ks, vs, r: int, scale: float) -> np.ndarray:
+def attend_one(q, kp, vp, valid: int, ks, vs, r: int, scale: float, causal: bool = False) -> np.ndarray:
     """One query row r of the suffix against prefix keys [0, valid) and the
-    suffix keys visible to r.  kp/vp: [L][dh], ks/vs: [S][dh]."""
+    suffix keys visible to r (causal: keys c <= r).  kp/vp: [L][dh], ks/vs: [S][dh]."""
     q, kp, vp, ks, vs = _f64(q), _f64(kp), _f64(vp), _f64(ks), _f64(vs)
     dh = q.size
     out = np.empty(dh, dtype=np.float64)
     _load().pi0o_attend_one(_p(q), dh, float(scale), _p(kp), _p(vp), int(valid), _p(ks), _p(vs),
-                            ks.shape[0], int(r), dh, _p(out))
+                            ks.shape[0], int(r), int(bool(causal)), dh, _p(out))
     return out
 
 
@@ -177,7 +193,7 @@ class Oracle:
             raise ValueError("prefix kv has the wrong size")
         return kv
 
-    def layer(self, l: int, h, kp, vp, valid: int, pos) -> np.ndarray:
+    def layer(self, l: int, h, kp, vp, valid: int, pos, causal: bool = False) -> np.ndarray:
         s = self.shape
         h = _f64(h).copy()
         kp, vp, pos = _f64(kp), _f64(vp), _f64(pos)
@@ -185,7 +201,7 @@ class Oracle:
         wl = self.w[l * layer_size:(l + 1) * layer_size]
         wl = np.ascontiguousarray(wl)
         _load().pi0o_expert_layer(ctypes.byref(self.cfg), _p(wl), _p(h), h.shape[0], _p(kp), _p(vp),
-                                  int(valid), _p(pos))
+                                  int(valid), _p(pos), int(bool(causal)))
         return h
 
     def _head_size(self):
@@ -200,19 +216,21 @@ class Oracle:
                                   _p(h))
         return h
 
-    def expert_forward(self, h, kv_sample, L: int, valid: int, pos_shift: float = 0.0) -> np.ndarray:
+    def expert_forward(self, h, kv_sample, L: int, valid: int, pos_shift: float = 0.0,
+                       causal: bool = False) -> np.ndarray:
         h = _f64(h).copy()
         kv = self._kv(kv_sample, L)
         _load().pi0o_expert_forward(ctypes.byref(self.cfg), _p(self.w), _p(h), _p(kv), int(L), int(valid),
-                                    float(pos_shift))
+                                    float(pos_shift), int(bool(causal)))
         return h
 
-    def velocity(self, state, x, t: float, kv_sample, L: int, valid: int, pos_shift: float = 0.0) -> np.ndarray:
+    def velocity(self, state, x, t: float, kv_sample, L: int, valid: int, pos_shift: float = 0.0,
+                 causal: bool = False) -> np.ndarray:
         s = self.shape
         v = np.empty((s.horizon, s.action_dim), dtype=np.float64)
         kv = self._kv(kv_sample, L)
         _load().pi0o_velocity(ctypes.byref(self.cfg), _p(self.w), _p(_f64(state)), _p(_f64(x)), float(t),
-                              _p(kv), int(L), int(valid), float(pos_shift), _p(v))
+                              _p(kv), int(L), int(valid), float(pos_shift), int(bool(causal)), _p(v))
         return v
 
     def denoise(self, state, noise, kv_sample, L: int, valid: int, num_steps: int,
@@ -225,17 +243,48 @@ class Oracle:
                              int(L), int(valid), int(num_steps), float(pos_shift), _p(out))
         return out
 
+    def denoise_ex(self, state, noise, kv_sample, L: int, valid: int, num_steps: int, schedule: str = "pi0",
+                   x_prediction: bool = False, causal: bool = False, dof_mask=None, padding=None,
+                   pos_shift: float = 0.0) -> np.ndarray:
+        """One sample with the Wall-X loop variants (page 3, generate_flow_action):
+        schedule "pi0" or "zero_to_one", x_prediction (v = head - noise), causal
+        suffix mask, and the first-step blend v = (padding - x)(1 - dof_mask) +
+        v dof_mask when padding is given (dof_mask, padding: [H][A])."""
+        s = self.shape
+        out = np.empty((s.horizon, s.action_dim), dtype=np.float64)
+        kv = self._kv(kv_sample, L)
+        if (dof_mask is None) != (padding is None):
+            raise ValueError("dof_mask and padding go together")
+        m = p = None
+        if padding is not None:
+            m = _f64(np.broadcast_to(dof_mask, out.shape))
+            p = _f64(np.broadcast_to(padding, out.shape))
+        _load().pi0o_denoise_ex(ctypes.byref(self.cfg), _p(self.w), _p(_f64(state)), _p(_f64(noise)), _p(kv),
+                                int(L), int(valid), int(num_steps), float(pos_shift), SCHEDULES[schedule],
+                                int(bool(x_prediction)), int(bool(causal)), _p(m) if m is not None else None,
+                                _p(p) if p is not None else None, _p(out))
+        return out
+
     def denoise_batch(self, inputs: dict, num_steps: int, samples=None, state_norm: dict | None = None,
-                      action_norm: dict | None = None) -> np.ndarray:
+                      action_norm: dict | None = None, options: dict | None = None) -> np.ndarray:
         """Run samples (default: all) of a batch laid out as the boundary takes it.
         state_norm / action_norm: the state is normalized before the loop and the
-        returned actions unnormalized (page 1, _normalize_state / _unnormalize_actions)."""
+        returned actions unnormalized (page 1, _normalize_state / _unnormalize_actions).
+        options: loop variants for denoise_ex (schedule, x_prediction, causal, and
+        per-batch dof_mask / padding arrays [B][H][A])."""
         kv = inputs["prefix_kv"]
         B, L = kv.shape[2], kv.shape[3]
         idx = range(B) if samples is None else samples
         outs = []
         for b in idx:
             state = apply_norm(inputs["state"][b], state_norm, inverse=False)
-            x = self.denoise(state, inputs["noise"][b], kv[:, :, b], L, int(inputs["valid_len"][b]), num_steps)
+            if options is None:
+                x = self.denoise(state, inputs["noise"][b], kv[:, :, b], L, int(inputs["valid_len"][b]), num_steps)
+            else:
+                o = dict(options)
+                m, p = o.pop("dof_mask", None), o.pop("padding", None)
+                x = self.denoise_ex(state, inputs["noise"][b], kv[:, :, b], L, int(inputs["valid_len"][b]),
+                                    num_steps, dof_mask=None if m is None else m[b],
+                                    padding=None if p is None else p[b], **o)
             outs.append(apply_norm(x, action_norm, inverse=True))
         return np.stack(outs)

@@ -13,7 +13,9 @@
  * denoise_step and sample_actions; the Gemma building blocks it calls
  * (GemmaRMSNorm with the (1 + w) scale, the gate/up/down GeGLU MLP with the
  * tanh GELU, rotate-half rotary embedding) are the Hugging Face Gemma ones
- * that page imports.
+ * that page imports.  The loop variants of pi0o_denoise_ex (0 -> 1 time grid,
+ * x-prediction head, dof-mask padding blend, causal action mask) follow page 3,
+ * the Wall-X modeling walk-through, generate_flow_action.
  *
  * Everything is computed in double precision with straightforward loops, one
  * sample at a time, in the order the page states the computation.  OpenMP
@@ -164,11 +166,15 @@ static void linear_rows(const double* W, const double* b, const double* X, int r
     }
 }
 
-/* Attention visibility inside the suffix (page 1, make_att_2d_masks applied to
- * embed_suffix's autoregressive mask [1, 1, 0, ..., 0]): key c is visible to
- * query r iff cumsum(ar)[c] <= cumsum(ar)[r].  All suffix tokens are real (no
- * suffix padding). */
-static int suffix_visible(int r, int c) {
+/* Attention visibility inside the suffix.  Default (page 1, make_att_2d_masks
+ * applied to embed_suffix's autoregressive mask [1, 1, 0, ..., 0]): key c is
+ * visible to query r iff cumsum(ar)[c] <= cumsum(ar)[r].  causal != 0 (page 3,
+ * the Wall-X modeling walk-through, generate_flow_action with
+ * causal_action_attention_mask set): the whole
+ * suffix-to-suffix block is replaced by a lower triangle, so key c is visible
+ * to query r iff c <= r.  All suffix tokens are real (no suffix padding). */
+static int suffix_visible(int r, int c, int causal) {
+  if (causal) return c <= r;
   /* cumsum of [1, 1, 0, 0, ...] is [1, 2, 2, 2, ...] */
   int cum_r = (r == 0) ? 1 : 2;
   int cum_c = (c == 0) ? 1 : 2;
@@ -179,10 +185,11 @@ static int suffix_visible(int r, int c) {
  * softmax(q k^T * scale + mask) v, masked keys get exactly zero weight).
  * Prefix keys j < valid are visible, keys j >= valid are padding and are not
  * read.  kp/vp: prefix keys/values of this query's kv head, row stride kstride.
- * ks/vs: suffix keys/values, row stride kstride.  r: suffix index of the query. */
+ * ks/vs: suffix keys/values, row stride kstride.  r: suffix index of the query;
+ * causal selects the suffix rule (suffix_visible). */
 void pi0o_attend_one(const double* q, int dh, double scale,
                      const double* kp, const double* vp, int valid,
-                     const double* ks, const double* vs, int S, int r,
+                     const double* ks, const double* vs, int S, int r, int causal,
                      size_t kstride, double* out) {
   int nk = valid + S;
   double* s = (double*)malloc(sizeof(double) * (size_t)nk);
@@ -191,7 +198,7 @@ void pi0o_attend_one(const double* q, int dh, double scale,
   for (int j = 0; j < nk; ++j) {
     const double* k;
     if (j < valid) { k = kp + (size_t)j * kstride; vis[j] = 1; }
-    else { int c = j - valid; k = ks + (size_t)c * kstride; vis[j] = (unsigned char)suffix_visible(r, c); }
+    else { int c = j - valid; k = ks + (size_t)c * kstride; vis[j] = (unsigned char)suffix_visible(r, c, causal); }
     if (!vis[j]) { s[j] = 0.0; continue; }
     double d = 0.0;
     for (int i = 0; i < dh; ++i) d += q[i] * k[i];
@@ -216,9 +223,10 @@ void pi0o_attend_one(const double* q, int dh, double scale,
  * of q and the suffix k at the rows' positions, attention over
  * [cached prefix K/V ; suffix K/V] with grouped kv heads, o_proj + residual,
  * post-attention norm, GeGLU MLP + residual.  h is updated in place.
- * kp/vp: this layer's prefix keys/values, [L][n_kv][dh], already rotated. */
+ * kp/vp: this layer's prefix keys/values, [L][n_kv][dh], already rotated.
+ * causal: suffix mask rule (suffix_visible). */
 void pi0o_expert_layer(const pi0o_cfg* c, const double* lw, double* h, int S,
-                       const double* kp, const double* vp, int valid, const double* pos) {
+                       const double* kp, const double* vp, int valid, const double* pos, int causal) {
   layer_offsets lo = layer_layout(c);
   int W = c->width, nh = c->num_heads, nkv = c->num_kv_heads, dh = c->head_dim, M = c->mlp_dim;
   int qd = nh * dh, kd = nkv * dh, group = nh / nkv;
@@ -246,7 +254,7 @@ void pi0o_expert_layer(const pi0o_cfg* c, const double* lw, double* h, int S,
       int gi = n / group;
       pi0o_attend_one(q + (size_t)r * qd + (size_t)n * dh, dh, scale,
                       kp + (size_t)gi * dh, vp + (size_t)gi * dh, valid,
-                      k + (size_t)gi * dh, v + (size_t)gi * dh, S, r,
+                      k + (size_t)gi * dh, v + (size_t)gi * dh, S, r, causal,
                       (size_t)kd, o + (size_t)r * qd + (size_t)n * dh);
     }
   linear_rows(lw + lo.wo, NULL, o, S, W, qd, t);
@@ -290,9 +298,10 @@ void pi0o_embed_suffix(const pi0o_cfg* c, const double* w, const double* state, 
  * suffix-only branch, without the final norm): h [S][W] in place.
  * kv: this sample's prefix cache [depth][2][L][n_kv][dh].  Positions continue
  * from the number of valid prefix tokens: pos_r = valid + r (+ pos_shift, a
- * test hook that shifts every suffix position; 0 in normal use). */
+ * test hook that shifts every suffix position; 0 in normal use).  causal:
+ * suffix mask rule (suffix_visible). */
 void pi0o_expert_forward(const pi0o_cfg* c, const double* w, double* h, const double* kv,
-                         int L, int valid, double pos_shift) {
+                         int L, int valid, double pos_shift, int causal) {
   layer_offsets lo = layer_layout(c);
   int S = 1 + c->horizon;
   size_t kd = (size_t)c->num_kv_heads * c->head_dim;
@@ -301,22 +310,22 @@ void pi0o_expert_forward(const pi0o_cfg* c, const double* w, double* h, const do
   for (int l = 0; l < c->depth; ++l) {
     const double* kp = kv + ((size_t)l * 2 + 0) * (size_t)L * kd;
     const double* vp = kv + ((size_t)l * 2 + 1) * (size_t)L * kd;
-    pi0o_expert_layer(c, w + (size_t)l * lo.size, h, S, kp, vp, valid, pos);
+    pi0o_expert_layer(c, w + (size_t)l * lo.size, h, S, kp, vp, valid, pos, causal);
   }
   free(pos);
 }
 
 /* Velocity v_t for one sample (page 1, denoise_step): embed the suffix, run the
  * expert, final norm on the action rows (the state row is dropped), then
- * action_out_proj.  v: [H][A]. */
+ * action_out_proj.  v: [H][A].  causal: suffix mask rule (suffix_visible). */
 void pi0o_velocity(const pi0o_cfg* c, const double* w, const double* state, const double* x, double t,
-                   const double* kv, int L, int valid, double pos_shift, double* v) {
+                   const double* kv, int L, int valid, double pos_shift, int causal, double* v) {
   head_offsets ho = head_layout(c);
   int W = c->width, H = c->horizon, A = c->action_dim, S = 1 + H;
   double* h = (double*)malloc(sizeof(double) * (size_t)S * W);
   double* hf = (double*)malloc(sizeof(double) * (size_t)H * W);
   pi0o_embed_suffix(c, w, state, x, t, h);
-  pi0o_expert_forward(c, w, h, kv, L, valid, pos_shift);
+  pi0o_expert_forward(c, w, h, kv, L, valid, pos_shift, causal);
   for (int i = 0; i < H; ++i) pi0o_rmsnorm(h + (size_t)(1 + i) * W, w + ho.final_norm, W, c->rms_eps, hf + (size_t)i * W);
   linear_rows(w + ho.aout_w, w + ho.aout_b, hf, H, A, W, v);
   free(h);
@@ -336,7 +345,7 @@ void pi0o_denoise(const pi0o_cfg* c, const double* w, const double* state, const
   memcpy(out, noise, sizeof(double) * n);
   for (int k = 0; k < num_steps; ++k) {
     double t = (double)(float)(1.0 + (double)k * dt);
-    pi0o_velocity(c, w, state, out, t, kv, L, valid, pos_shift, v);
+    pi0o_velocity(c, w, state, out, t, kv, L, valid, pos_shift, 0, v);
     for (size_t i = 0; i < n; ++i) out[i] = out[i] + dt * v[i];
   }
   free(v);
@@ -365,4 +374,53 @@ void pi0o_apply_norm(double* x, int n, int mode, const double* a, const double* 
 double pi0o_step_time(int k, int num_steps) {
   double dt = -1.0 / (double)num_steps;
   return (double)(float)(1.0 + (double)k * dt);
+}
+
+/* Time grid of the sampler, step k of N.  schedule 0 (page 1, sample_actions):
+ * t_k = 1 + k*dt with dt = -1/N, t stored as float32, every step advances by
+ * dt.  schedule 1 (the Wall-X flow-matching page, the Euler ODE integration of
+ * the flow head): the N + 1 points k/N from 0 to 1 held as float32; step k
+ * evaluates at t_k and advances by t_{k+1} - t_k (the Euler rule over
+ * consecutive grid points). */
+void pi0o_step_schedule(int k, int num_steps, int schedule, double* t, double* dt) {
+  if (schedule == 1) {
+    double t0 = (double)(float)((double)k / (double)num_steps);
+    double t1 = (double)(float)((double)(k + 1) / (double)num_steps);
+    *t = t0;
+    *dt = t1 - t0;
+  } else {
+    *dt = -1.0 / (double)num_steps;
+    *t = (double)(float)(1.0 + (double)k * *dt);
+  }
+}
+
+/* Euler sampler with the Wall-X loop variants (page 3, the Wall-X modeling
+ * walk-through, generate_flow_action: its first, prefill step and the later
+ * step_with_kvcache steps), for one sample:
+ *   x = noise; for k = 0..N-1: (t, dt) = pi0o_step_schedule(k, N, schedule);
+ *   y = head output at (x, t) with the suffix mask rule causal;
+ *   v = y - noise when x_pred (the head predicts the clean action; the noise
+ *       subtracted is the initial one), else v = y;
+ *   on the first step only, when padding != NULL:
+ *       v = (padding - x) * (1 - dof_mask) + v * dof_mask;
+ *   x = x + dt * v.
+ * dof_mask, padding: [H][A] (padding != NULL needs dof_mask != NULL).  out: [H][A]. */
+void pi0o_denoise_ex(const pi0o_cfg* c, const double* w, const double* state, const double* noise,
+                     const double* kv, int L, int valid, int num_steps, double pos_shift, int schedule,
+                     int x_pred, int causal, const double* dof_mask, const double* padding, double* out) {
+  int H = c->horizon, A = c->action_dim;
+  size_t n = (size_t)H * A;
+  double* v = (double*)malloc(sizeof(double) * n);
+  memcpy(out, noise, sizeof(double) * n);
+  for (int k = 0; k < num_steps; ++k) {
+    double t, dt;
+    pi0o_step_schedule(k, num_steps, schedule, &t, &dt);
+    pi0o_velocity(c, w, state, out, t, kv, L, valid, pos_shift, causal, v);
+    if (x_pred)
+      for (size_t i = 0; i < n; ++i) v[i] = v[i] - noise[i];
+    if (k == 0 && padding)
+      for (size_t i = 0; i < n; ++i) v[i] = (padding[i] - out[i]) * (1.0 - dof_mask[i]) + v[i] * dof_mask[i];
+    for (size_t i = 0; i < n; ++i) out[i] = out[i] + dt * v[i];
+  }
+  free(v);
 }

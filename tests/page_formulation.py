@@ -100,24 +100,28 @@ class PageFormulation:
         fused = self._linear("action_time_mlp_out", F.silu(self._linear("action_time_mlp_in", fused)))
         return torch.cat([state_tok, fused], dim=1)
 
-    def visibility(self, valid: torch.Tensor, L: int) -> torch.Tensor:
+    def visibility(self, valid: torch.Tensor, L: int, causal: bool = False) -> torch.Tensor:
         """bool [B, S, L + S]: prefix key j visible iff j < valid; suffix key c visible
-        to query r iff cumsum(ar)[c] <= cumsum(ar)[r] with ar = [1, 1, 0, ..., 0]."""
+        to query r iff cumsum(ar)[c] <= cumsum(ar)[r] with ar = [1, 1, 0, ..., 0].
+        causal: the suffix block is overwritten by a lower triangle, as page 3
+        (Wall-X, generate_flow_action) does under causal_action_attention_mask."""
         S = self.s.suffix_len
         B = valid.shape[0]
         pre = (torch.arange(L)[None, :] < valid[:, None])[:, None, :].expand(B, S, L)
         ar = torch.zeros(S, dtype=torch.int64)
         ar[:2] = 1
         cum = torch.cumsum(ar, 0)
-        suf = (cum[None, :] <= cum[:, None])[None].expand(B, S, S)
+        suf = (cum[None, :] <= cum[:, None])[None].expand(B, S, S).clone()
+        if causal:
+            suf[:, :, :] = torch.tril(torch.ones((S, S), dtype=torch.bool))
         return torch.cat([pre, suf], dim=2)
 
-    def velocity(self, state, x, t, kv, valid):
+    def velocity(self, state, x, t, kv, valid, causal: bool = False):
         """state [B, Sd], x [B, H, A], t [B], kv [depth, 2, B, L, n_kv, dh], valid [B] -> v [B, H, A]."""
         s = self.s
         B, L = kv.shape[2], kv.shape[3]
         h = self.suffix_embedding(state, x, t)
-        bias = torch.where(self.visibility(valid, L), 0.0, MASK_VALUE).to(torch.float64)[:, None]
+        bias = torch.where(self.visibility(valid, L, causal), 0.0, MASK_VALUE).to(torch.float64)[:, None]
         pos = valid[:, None].to(torch.int64) + torch.arange(s.suffix_len)[None, :]
         cos, sin = rope_tables_f64(pos, s.head_dim, s.rope_theta)
         rep = s.num_heads // s.num_kv_heads
@@ -151,4 +155,33 @@ class PageFormulation:
                 tk = float(np.float32(1.0 - k / num_steps))
                 v = self.velocity(state, x, torch.full((B,), tk, dtype=torch.float64), kv, valid)
                 x = x + (-1.0 / num_steps) * v
+        return x.numpy()
+
+    def denoise_wallx(self, inputs: dict, num_steps: int, x_pred: bool = False, causal: bool = False,
+                      dof_mask=None, padding=None) -> np.ndarray:
+        """The loop of page 3 (Wall-X, generate_flow_action) on this expert: a float32
+        time grid linspace(0, 1, N + 1); a first (prefill) step at times[0] whose
+        velocity takes the padding blend; then Euler over times[1:] with the
+        cached prefix.  x_pred: the head's output minus the initial noise."""
+        f = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
+        kv, valid = f(inputs["prefix_kv"]), torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
+        kv = torch.nan_to_num(kv, nan=0.0)
+        state, noise = f(inputs["state"]), f(inputs["noise"])
+        B = state.shape[0]
+        times = torch.linspace(0.0, 1.0, num_steps + 1, dtype=torch.float64).to(torch.float32).to(torch.float64)
+
+        def step(tk, x):
+            v = self.velocity(state, x, torch.full((B,), float(tk), dtype=torch.float64), kv, valid, causal)
+            return v - noise if x_pred else v
+
+        with torch.no_grad():
+            x = noise.clone()
+            v0 = step(times[0], x)
+            if padding is not None:
+                m = f(dof_mask)
+                if not bool((m == 1).all()):
+                    v0 = (f(padding) - x) * (1 - m) + v0 * m
+            x = x + (times[1] - times[0]) * v0
+            for i in range(1, num_steps):
+                x = x + (times[i + 1] - times[i]) * step(times[i], x)
         return x.numpy()
