@@ -138,6 +138,46 @@ pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len,
                               float* v_out, hipStream_t stream);
 
 /*
+ * The denoise loop with the loop variants of page 3 (the Wall-X modeling
+ * walk-through, generate_flow_action), on the same expert.  Arguments as
+ * pi0x_denoise; options == NULL, or all fields zero, is exactly pi0x_denoise.
+ *   schedule        PI0X_SCHEDULE_PI0: t_k = 1 + k*dt, dt = -1/num_steps
+ *                   (page 1, sample_actions).  PI0X_SCHEDULE_ZERO_TO_ONE:
+ *                   the float32 grid t_k = k/num_steps, k = 0..num_steps;
+ *                   step k evaluates at t_k and advances x by t_{k+1} - t_k,
+ *                   so t = 1 is never evaluated.
+ *   x_prediction    0: the head's output is the velocity.  1: the head
+ *                   predicts the clean chunk; v = output - noise, with the
+ *                   sample's initial noise.
+ *   causal_actions  0: the pi0 suffix mask (the state token sees itself,
+ *                   action tokens see the whole suffix).  1: suffix token s
+ *                   sees suffix tokens 0..s (a lower triangle).
+ *   dof_mask, padding_action  device float32 [batch][horizon][action_dim],
+ *                   both NULL or both set; read only, must not overlap
+ *                   actions_out.  When set, the first step's velocity becomes
+ *                   (padding_action - x)(1 - dof_mask) + v dof_mask, x being
+ *                   the noise; later steps are unchanged.
+ * The loop runs in the normalized action space: padding_action is taken as
+ * given, and the action unnormalization (pi0x_set_normalization) applies to
+ * the returned chunk only.  Errors as pi0x_denoise, plus
+ * PI0X_ERR_INVALID_ARG for an unknown schedule, flags other than 0 or 1, or
+ * only one of dof_mask / padding_action set.
+ */
+typedef enum { PI0X_SCHEDULE_PI0 = 0, PI0X_SCHEDULE_ZERO_TO_ONE = 1 } pi0x_schedule;
+typedef struct {
+  int32_t schedule;              /* pi0x_schedule */
+  int32_t x_prediction;          /* 0 or 1 */
+  int32_t causal_actions;        /* 0 or 1 */
+  const float* dof_mask;         /* device float32 [batch][horizon][action_dim] or NULL */
+  const float* padding_action;   /* device float32 [batch][horizon][action_dim] or NULL */
+} pi0x_loop_options;
+
+pi0x_status pi0x_denoise_ex(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                            const int32_t* prefix_valid_len, const float* state, const float* noise,
+                            int32_t num_steps, const pi0x_loop_options* options, float* actions_out,
+                            hipStream_t stream);
+
+/*
  * Boundary normalization (page 1, _build_norm_buffers and _apply_norm: the
  * LeRobot NormalizationMode semantics).  Statistics cover the first `count`
  * features; the remaining ones pass through unchanged.

@@ -16,7 +16,7 @@ def test_library_exports_every_declared_function():
     names = b.declared_functions()
     assert set(names) == {"pi0x_config_default", "pi0x_weight_count", "pi0x_expert_create", "pi0x_denoise",
                           "pi0x_denoise_step", "pi0x_expert_destroy", "pi0x_last_error", "pi0x_set_timing",
-                          "pi0x_read_timing", "pi0x_set_normalization"}
+                          "pi0x_read_timing", "pi0x_set_normalization", "pi0x_denoise_ex"}
     lib = b.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -83,6 +83,8 @@ def test_create_rejects_null_pointers():
 def test_calls_reject_null_handle():
     assert b.pi0x_denoise(None, 1, 8, 1, 1, 1, 1, 2, 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_denoise_step(None, 1, 8, 1, 1, 1, 1, 0.5, 1, None) == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_denoise_ex(None, 1, 8, 1, 1, 1, 1, 2, None, 1, None) == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_denoise_ex(None, 1, 8, 1, 1, 1, 1, 2, b.pi0x_loop_options(), 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_set_timing(None, 1) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_read_timing(None)[0] == b.PI0X_ERR_INVALID_ARG
     b.pi0x_expert_destroy(None)  # ignored
@@ -90,3 +92,11 @@ def test_calls_reject_null_handle():
 
 def test_set_normalization_null_handle():
     assert b.lib().pi0x_set_normalization(None, None, None) == b.PI0X_ERR_INVALID_ARG
+
+
+def test_loop_options_layout_matches_header():
+    # int32 schedule, x_prediction, causal_actions, then two pointers
+    o = b.pi0x_loop_options
+    assert o.schedule.offset == 0 and o.x_prediction.offset == 4 and o.causal_actions.offset == 8
+    assert o.dof_mask.offset == 16 and o.padding_action.offset == 24 and ctypes.sizeof(o) == 32
+    assert (b.PI0X_SCHEDULE_PI0, b.PI0X_SCHEDULE_ZERO_TO_ONE) == (0, 1)

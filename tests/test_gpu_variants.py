@@ -1,0 +1,246 @@
+"""Loop variants of page 3 (the Wall-X modeling walk-through,
+generate_flow_action) through pi0x_denoise_ex against the fp64 oracle's
+denoise_ex: the 0 -> 1 float32 time grid, the x-prediction head, the
+first-step dof-mask padding blend and the causal mask among suffix tokens.
+Bars as for the plain loop: float32 max|diff| <= 1e-4; bfloat16 max|diff|
+<= 3e-2 and relative L2 <= 1e-2."""
+from __future__ import annotations
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from vla_flow_matching_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TINY = synth.WORKLOADS["tiny_fp32_b1"]
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def check_close(gpu, ref, dtype, what=""):
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    err = float(np.max(np.abs(gpu - ref)))
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    _say(f"{what}: max|diff| {err:.3e} rel-L2 {rel:.3e}")
+    if dtype == "fp32":
+        assert err <= 1e-4, f"{what}: max|diff| {err}"
+    else:
+        assert err <= 3e-2 and rel <= 1e-2, f"{what}: max|diff| {err} rel-L2 {rel}"
+
+
+def _blend_inputs(seed, B, H, A):
+    """A LIBERO-like mask (leading dims active) with a few fractional entries, and a padding chunk."""
+    rng = np.random.default_rng(seed)
+    m = np.zeros((B, H, A), np.float32)
+    m[..., : A // 4] = 1.0
+    frac = rng.random((B, H, A)) < 0.1
+    m[frac] = rng.uniform(0.0, 1.0, int(frac.sum())).astype(np.float32)
+    p = rng.standard_normal((B, H, A)).astype(np.float32)
+    return m, p
+
+
+class Case:
+    def __init__(self, w: synth.Workload, norm_std=0.1, valid=None):
+        from vla_flow_matching_amd import binding
+        self.w = w
+        self.blob = synth.make_weights(w.shape, seed=w.seed, dtype=w.dtype, norm_std=norm_std)
+        self.inputs = synth.make_inputs(w)
+        if valid is not None:
+            self.inputs["valid_len"][:] = valid
+        cfg = binding.make_config(w.shape, w.dtype, max_batch=w.batch, max_prefix_len=max(w.prefix_len, 64),
+                                  max_steps=16)
+        _say(f"create {w.name} dtype={w.dtype} B={w.batch} L={w.prefix_len}")
+        self.ex = binding.Expert(cfg, self.blob)
+        self.dev = binding.device_inputs(self.inputs, w.dtype)
+        self.oracle = oracle.Oracle(w.shape, self.blob)
+        s = w.shape
+        self.mask, self.pad = _blend_inputs(w.seed + 100, w.batch, s.horizon, s.action_dim)
+        self.dmask = torch.from_numpy(self.mask).cuda()
+        self.dpad = torch.from_numpy(self.pad).cuda()
+
+    def run(self, n, schedule="pi0", x_prediction=False, causal=False, blend=False, out=None, noise=None):
+        d = self.dev
+        _say(f"denoise_ex {self.w.name} N={n} schedule={schedule} xpred={x_prediction} causal={causal} "
+             f"blend={blend}")
+        r = self.ex.denoise_ex(d["prefix_kv"], d["valid_len"], d["state"], d["noise"] if noise is None else noise,
+                               n, schedule=schedule, x_prediction=x_prediction, causal_actions=causal,
+                               dof_mask=self.dmask if blend else None, padding_action=self.dpad if blend else None,
+                               out=out)
+        torch.cuda.synchronize()
+        return r.cpu().numpy()
+
+    def ref(self, n, schedule="pi0", x_prediction=False, causal=False, blend=False, samples=None):
+        opts = dict(schedule=schedule, x_prediction=x_prediction, causal=causal,
+                    dof_mask=self.mask if blend else None, padding=self.pad if blend else None)
+        return self.oracle.denoise_batch(self.inputs, n, samples=samples, options=opts)
+
+    def close(self):
+        self.ex.close()
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = TINY.replace(name="tiny_variants", batch=3, seed=31)
+    c = Case(w, valid=[64, 23, 0])
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("schedule,x_prediction,causal,blend",
+                         [v for v in itertools.product(["pi0", "zero_to_one"], [False, True], [False, True],
+                                                       [False, True]) if any(v[1:]) or v[0] != "pi0"])
+def test_tiny_fp32_variant_parity(tiny, schedule, x_prediction, causal, blend):
+    n = 3
+    out = tiny.run(n, schedule, x_prediction, causal, blend)
+    check_close(out, tiny.ref(n, schedule, x_prediction, causal, blend), "fp32",
+                f"tiny fp32 {schedule} xpred={x_prediction} causal={causal} blend={blend}")
+
+
+def test_tiny_default_options_equal_denoise(tiny):
+    d = tiny.dev
+    plain = tiny.ex.denoise(d["prefix_kv"], d["valid_len"], d["state"], d["noise"], 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(tiny.run(3), plain.cpu().numpy())
+    from vla_flow_matching_amd import binding as b
+    out = torch.empty_like(d["noise"])
+    st = b.pi0x_denoise_ex(tiny.ex.h, 3, TINY.prefix_len, d["prefix_kv"].data_ptr(), d["valid_len"].data_ptr(),
+                           d["state"].data_ptr(), d["noise"].data_ptr(), 3, None, out.data_ptr(), None)
+    assert st == b.PI0X_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), plain.cpu().numpy())
+
+
+def test_tiny_variants_keep_their_own_graphs(tiny):
+    # each option set has its own captured graph: interleaving them changes nothing
+    a = tiny.run(3)
+    v = tiny.run(3, "zero_to_one", True, True, True)
+    assert np.array_equal(tiny.run(3), a)
+    assert np.array_equal(tiny.run(3, "zero_to_one", True, True, True), v)
+
+
+def test_tiny_x_prediction_output_may_alias_noise(tiny):
+    ref = tiny.run(4, "zero_to_one", True, False, True)
+    noise = tiny.dev["noise"].clone()
+    tiny.run(4, "zero_to_one", True, False, True, out=noise, noise=noise)
+    assert np.array_equal(noise.cpu().numpy(), ref)
+
+
+def test_tiny_single_step_blend_with_zero_mask_returns_padding(tiny):
+    # mask 0 everywhere, one step on the 0 -> 1 grid (dt = 1): x = noise + (p - noise)
+    saved = tiny.dmask
+    tiny.dmask = torch.zeros_like(saved)
+    try:
+        out = tiny.run(1, "zero_to_one", False, False, True)
+    finally:
+        tiny.dmask = saved
+    assert np.max(np.abs(out - tiny.pad)) <= 1e-5
+
+
+def test_tiny_new_blend_buffers_replay_same_graph(tiny):
+    ref = tiny.run(2, "zero_to_one", False, True, True)
+    m0, p0 = tiny.dmask, tiny.dpad
+    tiny.dmask, tiny.dpad = m0.clone(), p0.clone()
+    try:
+        assert np.array_equal(tiny.run(2, "zero_to_one", False, True, True), ref)
+    finally:
+        tiny.dmask, tiny.dpad = m0, p0
+
+
+def test_denoise_ex_rejects_bad_options(tiny):
+    from vla_flow_matching_amd import binding as b
+    d = tiny.dev
+    out = torch.empty_like(d["noise"])
+
+    def call(**kw):
+        o = b.pi0x_loop_options(kw.get("schedule", 0), kw.get("x_prediction", 0), kw.get("causal_actions", 0),
+                                kw.get("dof_mask"), kw.get("padding_action"))
+        return b.pi0x_denoise_ex(tiny.ex.h, 3, TINY.prefix_len, d["prefix_kv"].data_ptr(), d["valid_len"].data_ptr(),
+                                 d["state"].data_ptr(), d["noise"].data_ptr(), 2, o, out.data_ptr(), None)
+
+    assert call(schedule=2) == b.PI0X_ERR_INVALID_ARG
+    assert call(x_prediction=2) == b.PI0X_ERR_INVALID_ARG
+    assert call(causal_actions=-1) == b.PI0X_ERR_INVALID_ARG
+    assert call(dof_mask=tiny.dmask.data_ptr()) == b.PI0X_ERR_INVALID_ARG
+    assert call(padding_action=tiny.dpad.data_ptr()) == b.PI0X_ERR_INVALID_ARG
+    assert "dof_mask" in b.pi0x_last_error()
+    assert call(schedule=1, x_prediction=1, causal_actions=1) == b.PI0X_OK
+    torch.cuda.synchronize()
+
+
+def test_tiny_fp32_b8_tile_path_all_variants():
+    # 72 suffix rows: the float32 tile GEMMs with split K
+    w = TINY.replace(name="tiny_fp32_b8_variants", batch=8, seed=33)
+    c = Case(w, valid=[64, 63, 40, 33, 32, 31, 1, 0])
+    try:
+        check_close(c.run(3, "zero_to_one", True, True, True), c.ref(3, "zero_to_one", True, True, True), "fp32",
+                    "tiny fp32 B=8 all variants")
+    finally:
+        c.close()
+
+
+def test_tiny_bf16_b8_all_variants():
+    w = TINY.replace(name="tiny_bf16_b8_variants", dtype="bf16", batch=8, seed=35)
+    c = Case(w, valid=[64, 50, 17, 0, 64, 2, 33, 9])
+    try:
+        out = c.run(3, "zero_to_one", True, True, True)
+        ref = c.ref(3, "zero_to_one", True, True, True)
+        for b in range(w.batch):
+            check_close(out[b], ref[b], "bf16", f"tiny bf16 B=8 all variants, sample {b}")
+    finally:
+        c.close()
+
+
+def test_full_bf16_b1_variants():
+    # the full expert shape at batch 1 (the one-kernel wide GEMMs and split
+    # attention), three steps of the 0 -> 1 grid with the causal mask and the
+    # padding blend.  x-prediction is left to the float32 case below: with it
+    # the returned chunk on this grid is a weighted mean of head outputs with
+    # no noise term, so its relative L2 error is that of one bfloat16 head
+    # evaluation rather than of a loop output.
+    w = synth.WORKLOADS["pi0_bf16_b1"].replace(name="pi0_bf16_b1_variants", seed=37)
+    c = Case(w, norm_std=0.0)
+    try:
+        check_close(c.run(3, "zero_to_one", False, True, True), c.ref(3, "zero_to_one", False, True, True), "bf16",
+                    "pi0 bf16 B=1 zero_to_one+causal+blend N=3")
+    finally:
+        c.close()
+
+
+def test_full_fp32_b1_all_variants():
+    # float32 attention stages keys in blocks of 32, so the 51 suffix keys span
+    # two blocks and the causal limit crosses a block (and, at batch 1, split)
+    # boundary
+    w = synth.WORKLOADS["pi0_fp32_b1"].replace(name="pi0_fp32_b1_variants", seed=41)
+    c = Case(w, norm_std=0.0)
+    try:
+        check_close(c.run(2, "zero_to_one", True, True, True), c.ref(2, "zero_to_one", True, True, True),
+                    "fp32", "pi0 fp32 B=1 all variants N=2")
+    finally:
+        c.close()
+
+
+def test_full_bf16_b64_causal_sampled():
+    # batch 64 (the tile GEMMs, unsplit attention) with the causal mask on the
+    # pi0 grid, sampled samples against the oracle
+    w = synth.WORKLOADS["pi0_bf16_b64"].replace(name="pi0_bf16_b64_causal", seed=39)
+    c = Case(w, norm_std=0.0)
+    try:
+        out = c.run(2, "pi0", False, True, False)
+        samples = [0, 37, 63]
+        ref = c.ref(2, "pi0", False, True, False, samples=samples)
+        for i, b in enumerate(samples):
+            check_close(out[b], ref[i], "bf16", f"pi0 bf16 B=64 causal N=2, sample {b}")
+    finally:
+        c.close()

@@ -46,6 +46,16 @@ class pi0x_norm(ctypes.Structure):
                 ("a", ctypes.POINTER(ctypes.c_float)), ("b", ctypes.POINTER(ctypes.c_float))]
 
 
+PI0X_SCHEDULE_PI0 = 0
+PI0X_SCHEDULE_ZERO_TO_ONE = 1
+SCHEDULES = {"pi0": PI0X_SCHEDULE_PI0, "zero_to_one": PI0X_SCHEDULE_ZERO_TO_ONE}
+
+
+class pi0x_loop_options(ctypes.Structure):
+    _fields_ = [("schedule", ctypes.c_int32), ("x_prediction", ctypes.c_int32), ("causal_actions", ctypes.c_int32),
+                ("dof_mask", ctypes.c_void_p), ("padding_action", ctypes.c_void_p)]
+
+
 class Pi0xError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"pi0x status {status}: {msg}")
@@ -78,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.pi0x_expert_create.restype = i32
         L.pi0x_denoise.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp]
         L.pi0x_denoise.restype = i32
+        L.pi0x_denoise_ex.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(pi0x_loop_options), vp, vp]
+        L.pi0x_denoise_ex.restype = i32
         L.pi0x_denoise_step.argtypes = [vp, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp]
         L.pi0x_denoise_step.restype = i32
         L.pi0x_expert_destroy.argtypes = [vp]
@@ -117,6 +129,12 @@ def pi0x_expert_create(cfg: pi0x_config, weights_ptr: int, weights_bytes: int) -
 
 def pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream) -> int:
     return lib().pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream)
+
+
+def pi0x_denoise_ex(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, options, out, stream) -> int:
+    """options: a pi0x_loop_options or None."""
+    opt = ctypes.byref(options) if options is not None else None
+    return lib().pi0x_denoise_ex(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, opt, out, stream)
 
 
 def pi0x_denoise_step(h, batch, prefix_len, prefix_kv, valid, state, x_t, t, v_out, stream) -> int:
@@ -213,6 +231,22 @@ class Expert:
             out = torch.empty_like(noise)
         check(pi0x_denoise(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                            self._ptr(noise), int(num_steps), self._ptr(out), self._stream(stream)))
+        return out
+
+    def denoise_ex(self, prefix_kv, valid_len, state, noise, num_steps: int, schedule: str = "pi0",
+                   x_prediction: bool = False, causal_actions: bool = False, dof_mask=None, padding_action=None,
+                   out=None, stream=None):
+        """The loop variants of pi0x_denoise_ex; dof_mask / padding_action: float32
+        device tensors [B][H][A] (both or neither)."""
+        import torch
+        B = state.shape[0]
+        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
+        if out is None:
+            out = torch.empty_like(noise)
+        opts = pi0x_loop_options(SCHEDULES[schedule], int(bool(x_prediction)), int(bool(causal_actions)),
+                                 self._ptr(dof_mask), self._ptr(padding_action))
+        check(pi0x_denoise_ex(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
+                              self._ptr(noise), int(num_steps), opts, self._ptr(out), self._stream(stream)))
         return out
 
     def denoise_step(self, prefix_kv, valid_len, state, x_t, t: float, out=None, stream=None):

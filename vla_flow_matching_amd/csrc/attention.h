@@ -2,7 +2,9 @@
 // keys with the pi0 mask (page 1, _attend and make_att_2d_masks as used by
 // denoise_step): every suffix query sees the valid prefix keys j < valid_len;
 // inside the suffix the state token (s = 0) sees only itself and every action
-// token (s >= 1) sees the state token and all action tokens.  One kv head is
+// token (s >= 1) sees the state token and all action tokens.  With causal set
+// (page 3, Wall-X generate_flow_action under causal_action_attention_mask)
+// suffix token s sees suffix tokens 0..s instead.  One kv head is
 // shared by all query heads, so the num_heads * S queries of a sample (query
 // index qi = s*num_heads + n) form one matrix against one key/value sequence.
 //
@@ -45,6 +47,7 @@ struct AttnArgs {
   void* out;  // [B*S][ldo], head n of token s at column n*head_dim
   int ldo;
   float scale;
+  int causal;  // suffix mask: 0 pi0 block rule, 1 lower triangle
   int splits, tiles;
   float* partial;  // splits > 1: [B][tiles][splits][QT][2 + head_dim/4][threads], 512 per (query tile, field)
 };
@@ -234,11 +237,11 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
         for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t][kt]);
       }
     float sc[QT][KT][4];
-    // suffix blocks: the state token (query s = 0) sees only key 0
-    const int state_lim = pre ? lim : 1;
+    // suffix blocks: the state token (query s = 0) sees only key 0; with
+    // causal, query s sees keys 0..s
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      const int tlim = qs[t] >= 1 ? lim : min(lim, state_lim);
+      const int tlim = pre ? lim : (a.causal || qs[t] == 0) ? min(lim, qs[t] + 1) : lim;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll

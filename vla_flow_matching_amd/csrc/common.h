@@ -22,6 +22,8 @@ struct CallDesc {
   const float* x_in;     // denoise: the noise (x at t = 1); single step: x_t.  [B][H][A]
   float* out;            // denoise: the actions; single step: the velocity.  [B][H][A]
   float t;               // single step: the time value
+  const float* dof_mask;  // first-step padding blend (NULL: none), [B][H][A]
+  const float* padding;   // the padding action of that blend, [B][H][A]
 };
 
 // Boundary normalization statistics (page 1, _build_norm_buffers /

@@ -308,7 +308,13 @@ struct EpiGeglu {
 // v = acc + b_out[c]; mode 0: x <- x + dt v (x from desc->x_in on the first
 // step, else x_loop; written to x_loop and, on the last step, to desc->out
 // after the action unnormalization, page 1 _apply_norm inverse, when set);
-// mode 1: v is written to desc->out.
+// mode 1: v is written to desc->out.  Loop variants of page 3 (Wall-X,
+// generate_flow_action), mode 0 only: xpred takes the head output as the
+// predicted clean action, v = acc + b_out - noise (desc->x_in, the initial
+// noise); blend (set on the first step only) mixes in the padding action,
+// v = (p - x)(1 - m) + v m with m = desc->dof_mask, p = desc->padding.
+// Each output element is owned by one thread, which reads desc->x_in[i]
+// before it writes desc->out[i], so out may alias the noise.
 struct EpiEuler {
   static constexpr bool kPaired = false, kRowScale = true, kSsq = false;
   using Pre = float;  // the current x
@@ -319,6 +325,7 @@ struct EpiEuler {
   int from_input, write_out, mode;
   float dt;
   const NormDev* norm;  // action unnormalization of the returned chunk (write_out)
+  int xpred, blend;
   __device__ __forceinline__ int idx(int row, int col) const {
     const int b = row / S, s = row - b * S;
     return (s == 0 || col >= A) ? -1 : (b * H + s - 1) * A + col;
@@ -331,10 +338,15 @@ struct EpiEuler {
   __device__ __forceinline__ float one(int row, int col, float acc, Pre x) const {
     const int i = idx(row, col);
     if (i < 0) return 0.f;
-    const float v = acc + b_out[col];
+    float v = acc + b_out[col];
     if (mode == 1) {
       desc->out[i] = v;
     } else {
+      if (xpred) v -= desc->x_in[i];
+      if (blend) {
+        const float m = desc->dof_mask[i];
+        v = (desc->padding[i] - x) * (1.0f - m) + v * m;
+      }
       const float xn = x + dt * v;
       x_loop[i] = xn;
       if (write_out) desc->out[i] = unnorm_action(norm, col, xn);

@@ -82,9 +82,18 @@ struct Layer {
   void* wdown;  // [W][M]
 };
 
+// Loop variants of page 3 (Wall-X, generate_flow_action); all zero is the pi0
+// sampler of page 1.
+struct LoopOpts {
+  int zero_to_one = 0, xpred = 0, causal = 0, blend = 0;
+  int bits() const { return zero_to_one | xpred << 1 | causal << 2 | blend << 3; }
+};
+
 struct Key {
-  int B, L, N, mode;
-  bool operator<(const Key& o) const { return std::tie(B, L, N, mode) < std::tie(o.B, o.L, o.N, o.mode); }
+  int B, L, N, mode, opts;
+  bool operator<(const Key& o) const {
+    return std::tie(B, L, N, mode, opts) < std::tie(o.B, o.L, o.N, o.mode, o.opts);
+  }
 };
 
 uint16_t host_bf16(float f) {
@@ -386,7 +395,7 @@ inline int attn_splits(int B, int tiles, int nblk) {
 }
 
 template <typename T, int DH>
-pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer) {
+pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal) {
   constexpr int KB = AttnCfg<T>::KB;
   const int Lp = prefix_pad(L);
   AttnArgs a;
@@ -406,6 +415,7 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   a.out = h->o;
   a.ldo = h->qd;
   a.scale = 1.0f / std::sqrt((float)DH);
+  a.causal = causal;
   const int nq = h->nh * h->S;
   const int tiles = (nq + kAttnQueries - 1) / kAttnQueries;
   const int nblk = (L + KB - 1) / KB + (h->S + KB - 1) / KB;
@@ -442,12 +452,12 @@ pi0x_status allow_attn_smem(int dh) {
 }
 
 template <typename T>
-pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer) {
+pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal) {
   switch (h->dh) {
-    case 32: return launch_attn_dh<T, 32>(h, s, B, L, layer);
-    case 64: return launch_attn_dh<T, 64>(h, s, B, L, layer);
-    case 128: return launch_attn_dh<T, 128>(h, s, B, L, layer);
-    case 256: return launch_attn_dh<T, 256>(h, s, B, L, layer);
+    case 32: return launch_attn_dh<T, 32>(h, s, B, L, layer, causal);
+    case 64: return launch_attn_dh<T, 64>(h, s, B, L, layer, causal);
+    case 128: return launch_attn_dh<T, 128>(h, s, B, L, layer, causal);
+    case 256: return launch_attn_dh<T, 256>(h, s, B, L, layer, causal);
   }
   return fail(PI0X_ERR_SHAPE, "unsupported head_dim");
 }
@@ -465,12 +475,20 @@ pi0x_status launch_transpose_v(pi0x_expert* h, hipStream_t s, int B, int L) {
 // ---------------------------------------------------------------------------
 // The loop: N > 0 is the N-step sampler, N == 0 one velocity evaluation.
 // ---------------------------------------------------------------------------
+// Step size of step k of N: -1/N on the pi0 grid; t_{k+1} - t_k of the float32
+// grid points k/N on the 0 -> 1 grid (exact in float32: neighbouring points
+// are within a factor of two of each other).
+float step_dt(int k, int N, bool zero_to_one) {
+  if (N <= 0) return 0.f;
+  if (!zero_to_one) return (float)(-1.0 / (double)N);
+  return (float)((double)(k + 1) / (double)N) - (float)((double)k / (double)N);
+}
+
 template <typename T>
-pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
+pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const LoopOpts& lo) {
   const int W = h->W, S = h->S, H = h->H, R = B * S, AR = B * H;
   const int steps = N > 0 ? N : 1;
   const float eps = h->cfg.rms_eps;
-  const float dt = N > 0 ? (float)(-1.0 / (double)N) : 0.f;
   const bool bf = h->bf16();
   T* hb = bf ? reinterpret_cast<T*>(h->hb) : nullptr;
   // A operand of the norm-consuming projections: the residual stream itself
@@ -482,7 +500,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
   const NormIn nin{h->ssq, np};
 
   auto time_feats = [&]() -> pi0x_status {
-    hipLaunchKernelGGL((time_features_kernel<T>), dim3(steps), dim3(256), 0, s, h->desc, N, W,
+    hipLaunchKernelGGL((time_features_kernel<T>), dim3(steps), dim3(256), 0, s, h->desc, N, lo.zero_to_one, W,
                        (double)h->cfg.time_min_period, (double)h->cfg.time_max_period, (T*)h->tau);
     PI0X_HIP(hipGetLastError());
     return PI0X_OK;
@@ -526,7 +544,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
                                  EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, h->rope_cs,
                                                (T*)h->vts, h->Sp},
                                  nin)));
-      PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l));
+      PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l, lo.causal));
       PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
                                                      EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
       PI0X_TIMED(PI0X_KERNEL_GATE_UP,
@@ -535,17 +553,17 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N) {
                                                    EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
     }
     const int last = (k == steps - 1);
-    PI0X_TIMED(PI0X_KERNEL_FINAL,
-               (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W,
-                               EpiEuler{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1, dt, h->norm}, nin)));
+    const EpiEuler epi{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1,
+                       step_dt(k, N, lo.zero_to_one != 0), h->norm, lo.xpred, lo.blend && first};
+    PI0X_TIMED(PI0X_KERNEL_FINAL, (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W, epi, nin)));
   }
   return PI0X_OK;
 }
 
-pi0x_status run(pi0x_expert* h, int B, int L, int N, hipStream_t stream) {
-  const Key key{B, L, N, N > 0 ? 0 : 1};
+pi0x_status run(pi0x_expert* h, int B, int L, int N, const LoopOpts& lo, hipStream_t stream) {
+  const Key key{B, L, N, N > 0 ? 0 : 1, lo.bits()};
   auto launch_eager = [&](hipStream_t s) -> pi0x_status {
-    return h->bf16() ? enqueue<bf16>(h, s, B, L, N) : enqueue<float>(h, s, B, L, N);
+    return h->bf16() ? enqueue<bf16>(h, s, B, L, N, lo) : enqueue<float>(h, s, B, L, N, lo);
   };
   if (!h->cfg.use_graphs || h->timing) return launch_eager(stream);
   auto it = h->graphs.find(key);
@@ -913,13 +931,38 @@ pi0x_status pi0x_expert_create(const pi0x_config* cfg, const void* weights_host,
 pi0x_status pi0x_denoise(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
                          const int32_t* prefix_valid_len, const float* state, const float* noise, int32_t num_steps,
                          float* actions_out, hipStream_t stream) {
+  return pi0x_denoise_ex(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, noise, num_steps, nullptr,
+                         actions_out, stream);
+}
+
+pi0x_status pi0x_denoise_ex(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                            const int32_t* prefix_valid_len, const float* state, const float* noise,
+                            int32_t num_steps, const pi0x_loop_options* options, float* actions_out,
+                            hipStream_t stream) {
   PI0X_TRY(check_call(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, noise, actions_out));
   if (num_steps < 1) return fail(PI0X_ERR_INVALID_ARG, "num_steps must be >= 1");
   if (num_steps > h->cfg.max_steps) return fail(PI0X_ERR_CAPACITY, "num_steps exceeds max_steps");
+  LoopOpts lo;
+  const float *dof_mask = nullptr, *padding = nullptr;
+  if (options) {
+    if (options->schedule != PI0X_SCHEDULE_PI0 && options->schedule != PI0X_SCHEDULE_ZERO_TO_ONE)
+      return fail(PI0X_ERR_INVALID_ARG, "unknown schedule");
+    if ((options->x_prediction != 0 && options->x_prediction != 1) ||
+        (options->causal_actions != 0 && options->causal_actions != 1))
+      return fail(PI0X_ERR_INVALID_ARG, "x_prediction and causal_actions must be 0 or 1");
+    if ((options->dof_mask == nullptr) != (options->padding_action == nullptr))
+      return fail(PI0X_ERR_INVALID_ARG, "dof_mask and padding_action must both be set or both be NULL");
+    lo.zero_to_one = options->schedule == PI0X_SCHEDULE_ZERO_TO_ONE;
+    lo.xpred = options->x_prediction;
+    lo.causal = options->causal_actions;
+    lo.blend = options->padding_action != nullptr;
+    dof_mask = options->dof_mask;
+    padding = options->padding_action;
+  }
   hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, stream, h->desc, prefix_kv, prefix_valid_len, state, noise,
-                     actions_out, 0.f);
+                     actions_out, 0.f, dof_mask, padding);
   PI0X_HIP(hipGetLastError());
-  return run(h, batch, prefix_len, num_steps, stream);
+  return run(h, batch, prefix_len, num_steps, lo, stream);
 }
 
 pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
@@ -927,9 +970,9 @@ pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len,
                               float* v_out, hipStream_t stream) {
   PI0X_TRY(check_call(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, x_t, v_out));
   hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, stream, h->desc, prefix_kv, prefix_valid_len, state, x_t,
-                     v_out, t);
+                     v_out, t, nullptr, nullptr);
   PI0X_HIP(hipGetLastError());
-  return run(h, batch, prefix_len, 0, stream);
+  return run(h, batch, prefix_len, 0, LoopOpts{}, stream);
 }
 
 pi0x_status pi0x_set_normalization(pi0x_expert* h, const pi0x_norm* state, const pi0x_norm* action) {

@@ -8,13 +8,16 @@ namespace pi0x {
 
 // Writes the per-call descriptor (one thread).
 __global__ void set_desc_kernel(CallDesc* d, const void* kv, const int32_t* valid, const float* state,
-                                const float* x_in, float* out, float t) {
+                                const float* x_in, float* out, float t, const float* dof_mask,
+                                const float* padding) {
   d->kv = kv;
   d->valid = valid;
   d->state = state;
   d->x_in = x_in;
   d->out = out;
   d->t = t;
+  d->dof_mask = dof_mask;
+  d->padding = padding;
 }
 
 // State token of every sample (page 1, embed_suffix: state_proj(state)),
@@ -99,14 +102,17 @@ __global__ __launch_bounds__(256) void suffix_in_kernel(const CallDesc* __restri
 // per evaluated time: fraction_j = j/(W/2-1), period_j = min_p (max_p/min_p)^fraction_j,
 // tau = [sin(2 pi t / period) ; cos(2 pi t / period)], evaluated in float64 and
 // rounded once to the model dtype.  Denoise mode: row k uses t_k = 1 + k*dt with
-// dt = -1/N, rounded to float32 as the sampler stores it; single-step mode
+// dt = -1/N, rounded to float32 as the sampler stores it (page 1,
+// sample_actions), or with zero_to_one the float32 grid point k/N (page 3,
+// Wall-X generate_flow_action: a linspace grid from 0 to 1); single-step mode
 // (N == 0): one row with desc->t.
 template <typename T>
-__global__ void time_features_kernel(const CallDesc* __restrict__ desc, int N, int W, double min_p, double max_p,
-                                     T* __restrict__ tau) {
+__global__ void time_features_kernel(const CallDesc* __restrict__ desc, int N, int zero_to_one, int W, double min_p,
+                                     double max_p, T* __restrict__ tau) {
   const int k = blockIdx.x, half = W / 2;
   double t;
-  if (N > 0) t = (double)(float)(1.0 + (double)k * (-1.0 / (double)N));
+  if (N > 0 && zero_to_one) t = (double)(float)((double)k / (double)N);
+  else if (N > 0) t = (double)(float)(1.0 + (double)k * (-1.0 / (double)N));
   else t = (double)desc->t;
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
     const double frac = half > 1 ? (double)j / (double)(half - 1) : 0.0;
