@@ -71,6 +71,12 @@ def _load():
                                         ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D, _D]
         lib.pi0o_step_schedule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D]
         lib.pi0o_step_schedule.restype = None
+        lib.pi0o_prefill_weight_count.argtypes = [P]
+        lib.pi0o_prefill_weight_count.restype = ctypes.c_size_t
+        lib.pi0o_prefix_layer.argtypes = [P, _D, _D, ctypes.c_int, _D, _D, _D]
+        lib.pi0o_prefix_layer.restype = None
+        lib.pi0o_prefill.argtypes = [P, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_double, _D]
+        lib.pi0o_prefill.restype = None
         lib.pi0o_step_time.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.pi0o_step_time.restype = ctypes.c_double
         lib.pi0o_apply_norm.argtypes = [_D, ctypes.c_int, ctypes.c_int, _D, _D, ctypes.c_int, ctypes.c_int]
@@ -288,3 +294,50 @@ class Oracle:
                                     padding=None if p is None else p[b], **o)
             outs.append(apply_norm(x, action_norm, inverse=True))
         return np.stack(outs)
+
+
+class PrefillOracle:
+    """fp64 oracle of the prefix pass for one decoder-stack shape.  Weights are
+    the layers-only blob (synth.layer_layout order)."""
+
+    def __init__(self, shape, weights):
+        s = shape
+        self.shape = s
+        self.cfg = _Cfg(s.width, s.depth, s.mlp_dim, s.num_heads, s.num_kv_heads, s.head_dim,
+                        s.horizon, s.action_dim, s.state_dim, s.rms_eps, s.rope_theta,
+                        s.min_period, s.max_period)
+        n = _load().pi0o_prefill_weight_count(ctypes.byref(self.cfg))
+        w = _f64(weights)
+        if w.size != n:
+            raise ValueError(f"weight blob has {w.size} values, the shape needs {n}")
+        self.w = w
+
+    def layer(self, l: int, h, pos) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """One layer on real rows h [n][W] at positions pos [n]: (h_out, k, v)."""
+        s = self.shape
+        h = _f64(h).copy()
+        n = h.shape[0]
+        size = self.w.size // s.depth
+        wl = np.ascontiguousarray(self.w[l * size:(l + 1) * size])
+        k = np.empty((n, s.num_kv_heads * s.head_dim))
+        v = np.empty_like(k)
+        _load().pi0o_prefix_layer(ctypes.byref(self.cfg), _p(wl), _p(h), n, _p(_f64(pos)), _p(k), _p(v))
+        return h, k, v
+
+    def prefill(self, emb, valid: int, pos_shift: float = 0.0) -> np.ndarray:
+        """One sample: emb [L][W] -> cache [depth][2][L][n_kv][dh] (rows >= valid zero)."""
+        s = self.shape
+        emb = _f64(emb)
+        L = emb.shape[0]
+        out = np.empty((s.depth, 2, L, s.num_kv_heads, s.head_dim))
+        _load().pi0o_prefill(ctypes.byref(self.cfg), _p(self.w), _p(emb), int(L), int(valid), float(pos_shift),
+                             _p(out))
+        return out
+
+    def prefill_batch(self, inputs: dict, samples=None) -> np.ndarray:
+        """cache [depth][2][B][L][n_kv][dh] for the samples (default: all) of a batch
+        laid out as the boundary takes it."""
+        emb = inputs["embeddings"]
+        idx = range(emb.shape[0]) if samples is None else samples
+        outs = [self.prefill(emb[b], int(inputs["valid_len"][b])) for b in idx]
+        return np.stack(outs, axis=2)

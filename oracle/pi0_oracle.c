@@ -15,7 +15,10 @@
  * tanh GELU, rotate-half rotary embedding) are the Hugging Face Gemma ones
  * that page imports.  The loop variants of pi0o_denoise_ex (0 -> 1 time grid,
  * x-prediction head, dof-mask padding blend, causal action mask) follow page 3,
- * the Wall-X modeling walk-through, generate_flow_action.
+ * the Wall-X modeling walk-through, generate_flow_action.  The prefix pass of
+ * pi0o_prefill (the PaliGemma language model producing the per-layer K/V
+ * cache) follows page 1, _compute_layer_prefix_only and the prefix-only branch
+ * of PaliGemmaWithExpertModel.forward as sample_actions calls it.
  *
  * Everything is computed in double precision with straightforward loops, one
  * sample at a time, in the order the page states the computation.  OpenMP
@@ -423,4 +426,97 @@ void pi0o_denoise_ex(const pi0o_cfg* c, const double* w, const double* state, co
     for (size_t i = 0; i < n; ++i) out[i] = out[i] + dt * v[i];
   }
   free(v);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Prefix pass: the PaliGemma language model over the prefix embeddings       */
+/* ------------------------------------------------------------------------ */
+
+/* Values in a prefix-pass weight blob: depth decoder layers in the layer
+ * layout above (no final norm, no action head). */
+size_t pi0o_prefill_weight_count(const pi0o_cfg* c) { return layer_layout(c).size * (size_t)c->depth; }
+
+/* One language-model layer of the prefix pass (page 1,
+ * _compute_layer_prefix_only) on the n real prefix rows h [n][W], in place:
+ * pre-norm, q/k/v projections, rotary embedding of q and k at positions
+ * pos[r], attention of every row over every row (the prefix mask that
+ * make_att_2d_masks builds from an all-zero autoregressive mask: real tokens
+ * see each other both ways), o_proj + residual, post-attention norm, GeGLU
+ * MLP + residual.  k_out / v_out [n][n_kv][dh] receive the layer's post-RoPE
+ * keys and its values, the pair the suffix pass caches. */
+void pi0o_prefix_layer(const pi0o_cfg* c, const double* lw, double* h, int n, const double* pos,
+                       double* k_out, double* v_out) {
+  layer_offsets lo = layer_layout(c);
+  int W = c->width, nh = c->num_heads, nkv = c->num_kv_heads, dh = c->head_dim, M = c->mlp_dim;
+  int qd = nh * dh, kd = nkv * dh, group = nh / nkv;
+  double scale = 1.0 / sqrt((double)dh);
+  size_t rows = n > 0 ? (size_t)n : 1;
+  double* y = (double*)malloc(sizeof(double) * rows * W);
+  double* q = (double*)malloc(sizeof(double) * rows * qd);
+  double* o = (double*)malloc(sizeof(double) * rows * qd);
+  double* t = (double*)malloc(sizeof(double) * rows * W);
+  double* g = (double*)malloc(sizeof(double) * rows * M);
+  double* u = (double*)malloc(sizeof(double) * rows * M);
+
+  for (int r = 0; r < n; ++r) pi0o_rmsnorm(h + (size_t)r * W, lw + lo.in_norm, W, c->rms_eps, y + (size_t)r * W);
+  linear_rows(lw + lo.wq, NULL, y, n, qd, W, q);
+  linear_rows(lw + lo.wk, NULL, y, n, kd, W, k_out);
+  linear_rows(lw + lo.wv, NULL, y, n, kd, W, v_out);
+  for (int r = 0; r < n; ++r) {
+    for (int hh = 0; hh < nh; ++hh) pi0o_rope(q + (size_t)r * qd + (size_t)hh * dh, dh, pos[r], c->rope_theta);
+    for (int hh = 0; hh < nkv; ++hh) pi0o_rope(k_out + (size_t)r * kd + (size_t)hh * dh, dh, pos[r], c->rope_theta);
+  }
+  /* every row sees the n real keys: the "prefix" argument of pi0o_attend_one
+   * with no suffix keys */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int r = 0; r < n; ++r)
+    for (int hh = 0; hh < nh; ++hh) {
+      int gi = hh / group;
+      pi0o_attend_one(q + (size_t)r * qd + (size_t)hh * dh, dh, scale, k_out + (size_t)gi * dh,
+                      v_out + (size_t)gi * dh, n, NULL, NULL, 0, r, 0, (size_t)kd,
+                      o + (size_t)r * qd + (size_t)hh * dh);
+    }
+  linear_rows(lw + lo.wo, NULL, o, n, W, qd, t);
+  for (size_t i = 0; i < (size_t)n * W; ++i) h[i] += t[i];
+
+  for (int r = 0; r < n; ++r) pi0o_rmsnorm(h + (size_t)r * W, lw + lo.post_norm, W, c->rms_eps, y + (size_t)r * W);
+  linear_rows(lw + lo.wgate, NULL, y, n, M, W, g);
+  linear_rows(lw + lo.wup, NULL, y, n, M, W, u);
+  for (size_t i = 0; i < (size_t)n * M; ++i) g[i] = pi0o_gelu_tanh(g[i]) * u[i];
+  linear_rows(lw + lo.wdown, NULL, g, n, W, M, t);
+  for (size_t i = 0; i < (size_t)n * W; ++i) h[i] += t[i];
+
+  free(y); free(q); free(o); free(t); free(g); free(u);
+}
+
+/* Prefix pass of one sample (page 1: sample_actions builds the prefix masks and
+ * positions, PaliGemmaWithExpertModel.forward runs the prefix-only branch and
+ * keeps the per-layer cache).  emb [L][W]: the prefix embeddings, of which the
+ * first `valid` rows are real tokens and the rest padding (right padding, so
+ * positions cumsum(pad) - 1 are 0 .. valid-1, plus pos_shift, a test hook).
+ * Padded rows are masked out of every real row's attention, so the real rows
+ * are computed on their own.  kv_out [depth][2][L][n_kv][dh]: rows < valid get
+ * each layer's post-RoPE keys (index 0) and values (index 1); rows >= valid are
+ * set to 0 (their content is unspecified for the sampler, which never reads
+ * them).  The final norm only shapes the discarded prefix output and is not
+ * applied. */
+void pi0o_prefill(const pi0o_cfg* c, const double* w, const double* emb, int L, int valid, double pos_shift,
+                  double* kv_out) {
+  layer_offsets lo = layer_layout(c);
+  int W = c->width;
+  size_t kd = (size_t)c->num_kv_heads * c->head_dim;
+  int n = valid < 0 ? 0 : (valid > L ? L : valid);
+  memset(kv_out, 0, sizeof(double) * (size_t)c->depth * 2 * (size_t)L * kd);
+  if (n == 0) return;
+  double* h = (double*)malloc(sizeof(double) * (size_t)n * W);
+  double* pos = (double*)malloc(sizeof(double) * (size_t)n);
+  memcpy(h, emb, sizeof(double) * (size_t)n * W);
+  for (int r = 0; r < n; ++r) pos[r] = (double)r + pos_shift;
+  for (int l = 0; l < c->depth; ++l) {
+    double* k = kv_out + ((size_t)l * 2 + 0) * (size_t)L * kd;
+    double* v = kv_out + ((size_t)l * 2 + 1) * (size_t)L * kd;
+    pi0o_prefix_layer(c, w + (size_t)l * lo.size, h, n, pos, k, v);
+  }
+  free(h);
+  free(pos);
 }

@@ -35,14 +35,14 @@ from vla_flow_matching_amd import synth
 MASK_VALUE = -2.3819763e38
 
 
-def build_expert(shape: synth.ExpertShape, blob: np.ndarray) -> GemmaForCausalLM:
+def build_expert(shape: synth.ExpertShape, blob: np.ndarray, layout=synth.blob_layout) -> GemmaForCausalLM:
     cfg = GemmaConfig(head_dim=shape.head_dim, hidden_size=shape.width, intermediate_size=shape.mlp_dim,
                       num_attention_heads=shape.num_heads, num_hidden_layers=shape.depth,
                       num_key_value_heads=shape.num_kv_heads, vocab_size=16, rms_norm_eps=shape.rms_eps,
                       hidden_activation="gelu_pytorch_tanh", hidden_act="gelu_pytorch_tanh",
                       rope_parameters={"rope_theta": shape.rope_theta, "rope_type": "default"})
     m = GemmaForCausalLM(cfg).double().eval()
-    t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name), dtype=np.float64))
+    t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name, layout), dtype=np.float64))
     with torch.no_grad():
         for l, layer in enumerate(m.model.layers):
             layer.input_layernorm.weight.copy_(t(f"layers.{l}.input_norm"))
@@ -54,7 +54,8 @@ def build_expert(shape: synth.ExpertShape, blob: np.ndarray) -> GemmaForCausalLM
             layer.mlp.gate_proj.weight.copy_(t(f"layers.{l}.gate_proj"))
             layer.mlp.up_proj.weight.copy_(t(f"layers.{l}.up_proj"))
             layer.mlp.down_proj.weight.copy_(t(f"layers.{l}.down_proj"))
-        m.model.norm.weight.copy_(t("final_norm"))
+        if layout is synth.blob_layout:
+            m.model.norm.weight.copy_(t("final_norm"))
     return m
 
 
@@ -185,3 +186,47 @@ class PageFormulation:
             for i in range(1, num_steps):
                 x = x + (times[i + 1] - times[i]) * step(times[i], x)
         return x.numpy()
+
+
+class PrefixFormulation:
+    """The prefix pass of page 1 (sample_actions: embed_prefix's all-zero
+    autoregressive mask, make_att_2d_masks with the pad mask, positions
+    cumsum(pad) - 1; _compute_layer_prefix_only per layer) in whole-tensor
+    torch float64 with the Hugging Face Gemma modules, the additive mask bias
+    and an explicit repeat of the kv head."""
+
+    def __init__(self, shape: synth.ExpertShape, blob: np.ndarray):
+        self.s = shape
+        self.model = build_expert(shape, blob, layout=synth.layer_layout)
+
+    def prefill(self, inputs: dict) -> np.ndarray:
+        """cache [depth][2][B][L][n_kv][dh]: per layer the post-RoPE k and v."""
+        s = self.s
+        emb = torch.from_numpy(np.nan_to_num(np.array(inputs["embeddings"], dtype=np.float64), nan=0.0))
+        valid = torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
+        B, L, _ = emb.shape
+        pad = torch.arange(L)[None, :] < valid[:, None]
+        ar = torch.zeros((B, L), dtype=torch.int64)
+        cum = torch.cumsum(ar, dim=1)
+        att = (cum[:, None, :] <= cum[:, :, None]) & (pad[:, None, :] & pad[:, :, None])
+        bias = torch.where(att, 0.0, MASK_VALUE).to(torch.float64)[:, None]
+        pos = torch.cumsum(pad.to(torch.int64), dim=1) - 1
+        cos, sin = rope_tables_f64(pos, s.head_dim, s.rope_theta)
+        rep = s.num_heads // s.num_kv_heads
+        h = emb
+        cache = []
+        with torch.no_grad():
+            for layer in self.model.model.layers:
+                att_m = layer.self_attn
+                y = gemma_norm(h, layer.input_layernorm.weight, s.rms_eps)
+                q = att_m.q_proj(y).view(B, L, s.num_heads, s.head_dim).transpose(1, 2)
+                k = att_m.k_proj(y).view(B, L, s.num_kv_heads, s.head_dim).transpose(1, 2)
+                v = att_m.v_proj(y).view(B, L, s.num_kv_heads, s.head_dim).transpose(1, 2)
+                q, k = apply_rotary_pos_emb(q, k, cos, sin, unsqueeze_dim=1)
+                cache.append(torch.stack([k.transpose(1, 2), v.transpose(1, 2)]))  # [2, B, L, n_kv, dh]
+                kr, vr = k.repeat_interleave(rep, dim=1), v.repeat_interleave(rep, dim=1)
+                scores = q @ kr.transpose(-1, -2) / math.sqrt(s.head_dim) + bias
+                o = (torch.softmax(scores, dim=-1) @ vr).transpose(1, 2).reshape(B, L, -1)
+                h = h + att_m.o_proj(o)
+                h = h + layer.mlp(gemma_norm(h, layer.post_attention_layernorm.weight, s.rms_eps))
+        return torch.stack(cache).numpy()

@@ -16,7 +16,9 @@ as float32).
 Shapes follow the pi0 defaults (page 1: action horizon 50, action dim 32,
 48 text tokens, 224x224 images = 256 tokens per camera; get_gemma_config
 "gemma_300m" = width 1024, depth 18, mlp 4096, 8 query heads, 1 kv head,
-head_dim 256).
+head_dim 256; "gemma_2b" = width 2048, depth 18, mlp 16384, same heads for
+the prefix pass).  Prefix embeddings for the prefix pass are N(0, 1) like
+the prefix K/V.
 """
 from __future__ import annotations
 
@@ -50,6 +52,9 @@ class ExpertShape:
 GEMMA_300M = ExpertShape()
 TINY = ExpertShape(width=256, depth=2, mlp_dim=1024, num_heads=8, num_kv_heads=1, head_dim=32,
                    horizon=8, action_dim=32, state_dim=32)
+# the prefix pass (PaliGemma language model); only the layer fields matter
+GEMMA_2B = ExpertShape(width=2048, depth=18, mlp_dim=16384, num_heads=8, num_kv_heads=1, head_dim=256)
+TINY_VLM = ExpertShape(width=512, depth=3, mlp_dim=1536, num_heads=8, num_kv_heads=1, head_dim=64)
 
 
 @dataclass(frozen=True)
@@ -76,13 +81,29 @@ WORKLOADS = {
 }
 
 
-def blob_layout(s: ExpertShape) -> list[tuple[str, tuple[int, ...]]]:
-    """Tensor names and shapes of the flat weight blob, in blob order.
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    shape: ExpertShape
+    dtype: str
+    batch: int
+    prefix_len: int
+    ragged: bool = False  # per-sample valid length 512 + U{8..48}, else all valid
+    seed: int = 0
 
-    Matrices are [out_features][in_features] like nn.Linear weights.  Per layer:
-    input norm, q, k, v, o, post-attention norm, gate, up, down; then the final
-    norm; then state_proj, action_in_proj, action_time_mlp_in,
-    action_time_mlp_out, action_out_proj (weight, bias each)."""
+    def replace(self, **kw) -> "PrefillWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+PREFILL_WORKLOADS = {
+    "tiny_prefill_fp32": PrefillWorkload("tiny_prefill_fp32", TINY_VLM, "fp32", 1, 96),
+    "paligemma_bf16_b1": PrefillWorkload("paligemma_bf16_b1", GEMMA_2B, "bf16", 1, 816),
+}
+
+
+def layer_layout(s: ExpertShape) -> list[tuple[str, tuple[int, ...]]]:
+    """Per-layer tensors of a Gemma decoder stack in blob order: input norm, q,
+    k, v, o, post-attention norm, gate, up, down ([out][in] matrices)."""
     W, M = s.width, s.mlp_dim
     qd, kd = s.num_heads * s.head_dim, s.num_kv_heads * s.head_dim
     out = []
@@ -98,6 +119,18 @@ def blob_layout(s: ExpertShape) -> list[tuple[str, tuple[int, ...]]]:
             (f"layers.{l}.up_proj", (M, W)),
             (f"layers.{l}.down_proj", (W, M)),
         ]
+    return out
+
+
+def blob_layout(s: ExpertShape) -> list[tuple[str, tuple[int, ...]]]:
+    """Tensor names and shapes of the flat weight blob, in blob order.
+
+    Matrices are [out_features][in_features] like nn.Linear weights.  Per layer:
+    input norm, q, k, v, o, post-attention norm, gate, up, down; then the final
+    norm; then state_proj, action_in_proj, action_time_mlp_in,
+    action_time_mlp_out, action_out_proj (weight, bias each)."""
+    W = s.width
+    out = layer_layout(s)
     out += [
         ("final_norm", (W,)),
         ("state_proj.weight", (W, s.state_dim)),
@@ -114,9 +147,9 @@ def blob_layout(s: ExpertShape) -> list[tuple[str, tuple[int, ...]]]:
     return out
 
 
-def blob_offsets(s: ExpertShape) -> dict[str, tuple[int, tuple[int, ...]]]:
+def blob_offsets(s: ExpertShape, layout=blob_layout) -> dict[str, tuple[int, tuple[int, ...]]]:
     offs, p = {}, 0
-    for name, shp in blob_layout(s):
+    for name, shp in layout(s):
         offs[name] = (p, shp)
         p += int(np.prod(shp))
     return offs
@@ -126,8 +159,12 @@ def weight_count(s: ExpertShape) -> int:
     return sum(int(np.prod(shp)) for _, shp in blob_layout(s))
 
 
-def view(blob: np.ndarray, s: ExpertShape, name: str) -> np.ndarray:
-    off, shp = blob_offsets(s)[name]
+def prefill_weight_count(s: ExpertShape) -> int:
+    return sum(int(np.prod(shp)) for _, shp in layer_layout(s))
+
+
+def view(blob: np.ndarray, s: ExpertShape, name: str, layout=blob_layout) -> np.ndarray:
+    off, shp = blob_offsets(s, layout)[name]
     return blob[off:off + int(np.prod(shp))].reshape(shp)
 
 
@@ -154,15 +191,17 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 # tensor ids of the inputs (weights use their blob index)
-_ID_PREFIX_KV, _ID_STATE, _ID_NOISE, _ID_VALID = 100_001, 100_002, 100_003, 100_004
+_ID_PREFIX_KV, _ID_STATE, _ID_NOISE, _ID_VALID, _ID_EMB = 100_001, 100_002, 100_003, 100_004, 100_005
 
 
 def make_weights(s: ExpertShape, seed: int = 0, dtype: str = "fp32", std: float = 0.02,
-                 norm_std: float = 0.0) -> np.ndarray:
-    """Flat float32 weight blob.  Norm weights are N(0, norm_std) (0 by default)."""
-    blob = np.empty(weight_count(s), dtype=np.float32)
+                 norm_std: float = 0.0, layout=blob_layout) -> np.ndarray:
+    """Flat float32 weight blob.  Norm weights are N(0, norm_std) (0 by default).
+    layout=layer_layout gives the prefix-pass blob (decoder layers only)."""
+    entries = layout(s)
+    blob = np.empty(sum(int(np.prod(shp)) for _, shp in entries), dtype=np.float32)
     p = 0
-    for tid, (name, shp) in enumerate(blob_layout(s)):
+    for tid, (name, shp) in enumerate(entries):
         n = int(np.prod(shp))
         if name.endswith("norm"):
             if norm_std == 0.0:
@@ -177,7 +216,12 @@ def make_weights(s: ExpertShape, seed: int = 0, dtype: str = "fp32", std: float 
     return blob
 
 
-def make_valid_len(w: Workload) -> np.ndarray:
+def make_prefill_weights(s: ExpertShape, seed: int = 0, dtype: str = "fp32", std: float = 0.02,
+                         norm_std: float = 0.0) -> np.ndarray:
+    return make_weights(s, seed, dtype, std, norm_std, layout=layer_layout)
+
+
+def make_valid_len(w) -> np.ndarray:
     if not w.ragged:
         return np.full(w.batch, w.prefix_len, dtype=np.int32)
     # 2 cameras (2 x 256 image tokens) + text of valid length U{8..48}
@@ -196,3 +240,13 @@ def make_inputs(w: Workload) -> dict[str, np.ndarray]:
     state = _rng(w.seed, _ID_STATE).standard_normal((w.batch, s.state_dim), dtype=np.float32)
     noise = _rng(w.seed, _ID_NOISE).standard_normal((w.batch, s.horizon, s.action_dim), dtype=np.float32)
     return {"prefix_kv": kv, "valid_len": make_valid_len(w), "state": state, "noise": noise}
+
+
+def make_prefill_inputs(w: PrefillWorkload) -> dict[str, np.ndarray]:
+    """embeddings [B][L][width] float32 (bf16-rounded for bf16), valid_len [B] int32."""
+    s = w.shape
+    shp = (w.batch, w.prefix_len, s.width)
+    emb = _rng(w.seed, _ID_EMB).standard_normal(int(np.prod(shp)), dtype=np.float32).reshape(shp)
+    if w.dtype == "bf16":
+        emb = round_bf16(emb).reshape(shp)
+    return {"embeddings": emb, "valid_len": make_valid_len(w)}
