@@ -223,7 +223,8 @@ const char* pi0x_last_error(void);
  * counts (arrays of PI0X_KERNEL_CLASSES entries) and clears the record.
  */
 typedef enum {
-  PI0X_KERNEL_SUFFIX_EMBED = 0, /* time features, state token, time MLP */
+  PI0X_KERNEL_SUFFIX_EMBED = 0, /* time features, state token, time MLP (prefix pass: the
+                                   embedding copy and the rotary positions) */
   PI0X_KERNEL_RMSNORM = 1,      /* (unused: the norms are fused into the projections) */
   PI0X_KERNEL_QKV_ROPE = 2,     /* q/k/v projection + RoPE */
   PI0X_KERNEL_ATTENTION = 3,    /* prefix + suffix GQA attention (and the per-call transpose
@@ -237,6 +238,72 @@ typedef enum {
 
 pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable);
 pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches);
+
+/*
+ * The prefix pass (page 1: sample_actions builds the prefix masks and
+ * positions and runs the prefix-only branch of
+ * PaliGemmaWithExpertModel.forward, _compute_layer_prefix_only per layer),
+ * producing the cache pi0x_denoise reads.  The handle holds a PaliGemma
+ * language-model decoder stack (get_gemma_config "gemma_2b": width 2048,
+ * depth 18, mlp 16384, 8 query heads, 1 kv head, head_dim 256).  The image
+ * and text embedding (SigLIP, the projector, the token table and its
+ * sqrt(width) scale) happens before this boundary: it takes the prefix
+ * embeddings.  Of the config, only the layer fields (width .. head_dim,
+ * rms_eps, rope_theta), dtype, use_graphs, max_batch and max_prefix_len
+ * apply; max_batch * max_prefix_len <= 65536 rows.
+ *
+ * Weight blob: float32, depth decoder layers in the per-layer order of
+ * pi0x_expert_create (input_norm, q, k, v, o, post_norm, gate, up, down,
+ * nn.Linear [out][in] layout); no final norm and no action head.
+ */
+typedef struct pi0x_prefix_model pi0x_prefix_model;
+
+/* Gemma-2B layer fields, max_batch 1, max_prefix_len 1024, bfloat16, graphs on. */
+void pi0x_prefix_config_default(pi0x_config* cfg);
+
+/* Number of float32 values in a prefix-pass weight blob (0 for a NULL or
+ * non-positive config). */
+size_t pi0x_prefix_weight_count(const pi0x_config* cfg);
+
+/* Creates a prefix-pass handle on the current HIP device (synchronous; the
+ * blob is copied, repacked and converted as in pi0x_expert_create).  Errors
+ * as pi0x_expert_create, plus PI0X_ERR_CAPACITY when max_batch *
+ * max_prefix_len exceeds 65536.  On error *out is NULL. */
+pi0x_status pi0x_prefix_create(const pi0x_config* cfg, const void* weights_host, size_t weights_bytes,
+                               pi0x_prefix_model** out);
+
+/*
+ * Runs the prefix pass.
+ *   prefix_embeddings  device, cfg dtype, [batch][prefix_len][width]: the
+ *                      embedded image and text tokens.  Read only.
+ *   prefix_valid_len   device int32 [batch]: tokens [0, v) are real and
+ *                      [v, prefix_len) padding (right padding, so the real
+ *                      tokens sit at positions 0 .. v-1, page 1's
+ *                      cumsum(pad) - 1).  Values outside [0, prefix_len] are
+ *                      clamped into it.  Padding never reaches a real token.
+ *   prefix_kv_out      device, cfg dtype, [depth][2][batch][prefix_len][head_dim],
+ *                      16-byte aligned: per layer the post-RoPE keys (index 0)
+ *                      and the values (index 1) of the single kv head -- the
+ *                      prefix_kv argument of pi0x_denoise for the same batch,
+ *                      prefix_len and prefix_valid_len.  Rows >= v of a sample
+ *                      are written with unspecified values (pi0x_denoise never
+ *                      reads them).  Must not overlap the embeddings.
+ * Real tokens attend to every real token (the prefix mask is bidirectional).
+ * Asynchronous on stream; one handle serves one stream at a time.
+ * prefix_len == 0 returns PI0X_OK without work.  Errors: PI0X_ERR_INVALID_ARG
+ * for NULL pointers, batch < 1, a negative prefix_len, a misaligned
+ * prefix_kv_out or another current device; PI0X_ERR_CAPACITY above the
+ * handle's max_batch or max_prefix_len; PI0X_ERR_HIP for launch errors.
+ */
+pi0x_status pi0x_prefill(pi0x_prefix_model* p, int32_t batch, int32_t prefix_len, const void* prefix_embeddings,
+                         const int32_t* prefix_valid_len, void* prefix_kv_out, hipStream_t stream);
+
+/* Releases the handle (synchronises the device first); NULL is ignored. */
+void pi0x_prefix_destroy(pi0x_prefix_model* p);
+
+/* Kernel timing of the prefix pass, as pi0x_set_timing / pi0x_read_timing. */
+pi0x_status pi0x_prefix_set_timing(pi0x_prefix_model* p, int32_t enable);
+pi0x_status pi0x_prefix_read_timing(pi0x_prefix_model* p, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,10 @@ def test_library_exports_every_declared_function():
     names = b.declared_functions()
     assert set(names) == {"pi0x_config_default", "pi0x_weight_count", "pi0x_expert_create", "pi0x_denoise",
                           "pi0x_denoise_step", "pi0x_expert_destroy", "pi0x_last_error", "pi0x_set_timing",
-                          "pi0x_read_timing", "pi0x_set_normalization", "pi0x_denoise_ex"}
+                          "pi0x_read_timing", "pi0x_set_normalization", "pi0x_denoise_ex",
+                          "pi0x_prefix_config_default", "pi0x_prefix_weight_count", "pi0x_prefix_create",
+                          "pi0x_prefill", "pi0x_prefix_destroy", "pi0x_prefix_set_timing",
+                          "pi0x_prefix_read_timing"}
     lib = b.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -100,3 +103,42 @@ def test_loop_options_layout_matches_header():
     assert o.schedule.offset == 0 and o.x_prediction.offset == 4 and o.causal_actions.offset == 8
     assert o.dof_mask.offset == 16 and o.padding_action.offset == 24 and ctypes.sizeof(o) == 32
     assert (b.PI0X_SCHEDULE_PI0, b.PI0X_SCHEDULE_ZERO_TO_ONE) == (0, 1)
+
+
+def test_prefix_config_default_is_gemma_2b():
+    c = b.pi0x_prefix_config_default()
+    assert (c.width, c.depth, c.mlp_dim, c.num_heads, c.num_kv_heads, c.head_dim) == (2048, 18, 16384, 8, 1, 256)
+    assert c.dtype == b.PI0X_BF16 and c.max_batch == 1 and c.max_prefix_len == 1024
+
+
+@pytest.mark.parametrize("shape", [synth.GEMMA_2B, synth.TINY_VLM])
+def test_prefix_weight_count_matches_layer_layout(shape):
+    assert b.pi0x_prefix_weight_count(b.make_config(shape)) == synth.prefill_weight_count(shape)
+
+
+def test_prefix_weight_count_gemma_2b():
+    # 18 layers x (2 norms of 2048 + q/o 2 x 2048^2 + k/v 2 x 256 x 2048 + 3 x 16384 x 2048)
+    assert synth.prefill_weight_count(synth.GEMMA_2B) == 18 * (2 * 2048 + 2 * 2048 * 2048 + 2 * 256 * 2048
+                                                               + 3 * 16384 * 2048)
+
+
+def test_prefix_create_rejects_bad_config_and_blob():
+    cfg = b.make_config(synth.TINY_VLM, "fp32", max_batch=2, max_prefix_len=64)
+    w = np.zeros(16, np.float32)
+    st, h = b.pi0x_prefix_create(cfg, w.ctypes.data, w.nbytes)
+    assert st == b.PI0X_ERR_SHAPE and h == 0 and "weights_bytes" in b.pi0x_last_error()
+    big = b.make_config(synth.TINY_VLM, "fp32", max_batch=128, max_prefix_len=1024)
+    st, h = b.pi0x_prefix_create(big, w.ctypes.data, w.nbytes)
+    assert st == b.PI0X_ERR_CAPACITY and h == 0
+    bad = b.make_config(synth.TINY_VLM, "fp32")
+    bad.head_dim = 48
+    assert b.pi0x_prefix_create(bad, w.ctypes.data, w.nbytes)[0] == b.PI0X_ERR_SHAPE
+    h = ctypes.c_void_p()
+    assert b.lib().pi0x_prefix_create(None, None, 0, ctypes.byref(h)) == b.PI0X_ERR_INVALID_ARG
+
+
+def test_prefix_calls_reject_null_handle():
+    assert b.pi0x_prefill(None, 1, 8, 1, 1, 16, None) == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_prefix_set_timing(None, 1) == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_prefix_read_timing(None)[0] == b.PI0X_ERR_INVALID_ARG
+    b.pi0x_prefix_destroy(None)  # ignored

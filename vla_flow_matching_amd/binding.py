@@ -102,6 +102,20 @@ def lib() -> ctypes.CDLL:
         L.pi0x_set_timing.restype = i32
         L.pi0x_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.pi0x_read_timing.restype = i32
+        L.pi0x_prefix_config_default.argtypes = [P]
+        L.pi0x_prefix_config_default.restype = None
+        L.pi0x_prefix_weight_count.argtypes = [P]
+        L.pi0x_prefix_weight_count.restype = sz
+        L.pi0x_prefix_create.argtypes = [P, vp, sz, ctypes.POINTER(vp)]
+        L.pi0x_prefix_create.restype = i32
+        L.pi0x_prefill.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.pi0x_prefill.restype = i32
+        L.pi0x_prefix_destroy.argtypes = [vp]
+        L.pi0x_prefix_destroy.restype = None
+        L.pi0x_prefix_set_timing.argtypes = [vp, i32]
+        L.pi0x_prefix_set_timing.restype = i32
+        L.pi0x_prefix_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.pi0x_prefix_read_timing.restype = i32
         _lib = L
     return _lib
 
@@ -143,6 +157,41 @@ def pi0x_denoise_step(h, batch, prefix_len, prefix_kv, valid, state, x_t, t, v_o
 
 def pi0x_expert_destroy(h) -> None:
     lib().pi0x_expert_destroy(h)
+
+
+def pi0x_prefix_config_default() -> pi0x_config:
+    c = pi0x_config()
+    lib().pi0x_prefix_config_default(ctypes.byref(c))
+    return c
+
+
+def pi0x_prefix_weight_count(cfg: pi0x_config) -> int:
+    return lib().pi0x_prefix_weight_count(ctypes.byref(cfg))
+
+
+def pi0x_prefix_create(cfg: pi0x_config, weights_ptr: int, weights_bytes: int) -> tuple[int, int]:
+    h = ctypes.c_void_p()
+    st = lib().pi0x_prefix_create(ctypes.byref(cfg), weights_ptr, weights_bytes, ctypes.byref(h))
+    return st, (h.value or 0)
+
+
+def pi0x_prefill(p, batch, prefix_len, embeddings, valid, kv_out, stream) -> int:
+    return lib().pi0x_prefill(p, batch, prefix_len, embeddings, valid, kv_out, stream)
+
+
+def pi0x_prefix_destroy(p) -> None:
+    lib().pi0x_prefix_destroy(p)
+
+
+def pi0x_prefix_set_timing(p, enable: bool) -> int:
+    return lib().pi0x_prefix_set_timing(p, int(bool(enable)))
+
+
+def pi0x_prefix_read_timing(p) -> tuple[int, dict]:
+    tot = (ctypes.c_double * len(KERNEL_CLASSES))()
+    cnt = (ctypes.c_int64 * len(KERNEL_CLASSES))()
+    st = lib().pi0x_prefix_read_timing(p, tot, cnt)
+    return st, {k: (tot[i], int(cnt[i])) for i, k in enumerate(KERNEL_CLASSES)}
 
 
 KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final"]
@@ -295,4 +344,55 @@ def device_inputs(inputs: dict, dtype: str, device: str = "cuda"):
         "valid_len": torch.from_numpy(np.ascontiguousarray(inputs["valid_len"], dtype=np.int32)).to(device),
         "state": torch.from_numpy(np.ascontiguousarray(inputs["state"], dtype=np.float32)).to(device),
         "noise": torch.from_numpy(np.ascontiguousarray(inputs["noise"], dtype=np.float32)).to(device),
+    }
+
+
+class PrefixModel:
+    """Owns a pi0x prefix-pass handle; calls take torch device tensors."""
+
+    def __init__(self, cfg: pi0x_config, weights: np.ndarray):
+        import torch  # noqa: F401
+        w = np.ascontiguousarray(weights, dtype=np.float32)
+        self.cfg = cfg
+        st, self.h = pi0x_prefix_create(cfg, w.ctypes.data, w.nbytes)
+        check(st)
+
+    def prefill(self, embeddings, valid_len, out=None, stream=None):
+        """embeddings [B][L][width] (model dtype) -> cache [depth][2][B][L][head_dim]."""
+        import torch
+        B, L = embeddings.shape[0], embeddings.shape[1]
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.depth, 2, B, L, c.head_dim), dtype=embeddings.dtype, device=embeddings.device)
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        check(pi0x_prefill(self.h, B, L, embeddings.data_ptr(), valid_len.data_ptr(), out.data_ptr(), s))
+        return out
+
+    def set_timing(self, enable: bool):
+        check(pi0x_prefix_set_timing(self.h, enable))
+
+    def read_timing(self) -> dict:
+        st, t = pi0x_prefix_read_timing(self.h)
+        check(st)
+        return t
+
+    def close(self):
+        if getattr(self, "h", 0):
+            pi0x_prefix_destroy(self.h)
+            self.h = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def prefill_device_inputs(inputs: dict, dtype: str, device: str = "cuda"):
+    """Host prefix-pass inputs (synth.make_prefill_inputs) as device tensors."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {
+        "embeddings": torch.from_numpy(np.ascontiguousarray(inputs["embeddings"])).to(device=device, dtype=tdt),
+        "valid_len": torch.from_numpy(np.ascontiguousarray(inputs["valid_len"], dtype=np.int32)).to(device),
     }

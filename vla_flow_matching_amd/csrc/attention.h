@@ -4,7 +4,15 @@
 // inside the suffix the state token (s = 0) sees only itself and every action
 // token (s >= 1) sees the state token and all action tokens.  With causal set
 // (page 3, Wall-X generate_flow_action under causal_action_attention_mask)
-// suffix token s sees suffix tokens 0..s instead.  One kv head is
+// suffix token s sees suffix tokens 0..s instead.
+//
+// Prefix pass (prefill set; page 1, _compute_layer_prefix_only under the
+// prefix mask make_att_2d_masks builds from an all-zero autoregressive mask):
+// the S queries per sample are the prefix tokens themselves and there are no
+// suffix keys; every query sees the keys j < valid_len, which this layer's
+// q/k/v epilogue has just written to the cache (desc->kv) and, transposed, to
+// vtp.  Padded queries are computed like real ones (their rows are never
+// read); with valid_len 0 they see no key and get a zero output.  One kv head is
 // shared by all query heads, so the num_heads * S queries of a sample (query
 // index qi = s*num_heads + n) form one matrix against one key/value sequence.
 //
@@ -48,6 +56,7 @@ struct AttnArgs {
   int ldo;
   float scale;
   int causal;  // suffix mask: 0 pi0 block rule, 1 lower triangle
+  int prefill;  // prefix pass: prefix keys only
   int splits, tiles;
   float* partial;  // splits > 1: [B][tiles][splits][QT][2 + head_dim/4][threads], 512 per (query tile, field)
 };
@@ -130,7 +139,10 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
   const T* Vts = reinterpret_cast<const T*>(a.vts) + (size_t)b * DH * a.Sp;
   const T* Sq = qk + (size_t)b * a.S * a.ldqk;
 
-  const int nb_pre = (valid + KB - 1) / KB, nb_suf = (a.S + KB - 1) / KB;
+  // (at least one block, so that a prefix pass with no real key still stages
+  // an in-bounds block; its keys are all masked)
+  const int nb_pre = a.prefill ? max((valid + KB - 1) / KB, 1) : (valid + KB - 1) / KB;
+  const int nb_suf = a.prefill ? 0 : (a.S + KB - 1) / KB;
   const int nblk = nb_pre + nb_suf;
   const int blk_b = (int)((long)split * nblk / a.splits), blk_e = (int)((long)(split + 1) * nblk / a.splits);
 
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
       continue;
     }
     if (!qok[t]) continue;
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // 0: a prefix-pass query with no real key
     T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs[t]) * a.ldo + qn[t] * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] += w * v[2 + e];
   }
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
   for (int e = 0; e < 4; ++e) orow[d0 * 16 + g * 4 + e] = from_f32<T>(o[e] * inv);

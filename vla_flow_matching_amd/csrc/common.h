@@ -24,6 +24,10 @@ struct CallDesc {
   float t;               // single step: the time value
   const float* dof_mask;  // first-step padding blend (NULL: none), [B][H][A]
   const float* padding;   // the padding action of that blend, [B][H][A]
+  // prefix pass: the embeddings [B][L][width] (model dtype) and the cache it
+  // writes, [depth][2][B][L][head_dim] (kv points at the same cache)
+  const void* emb;
+  void* kv_out;
 };
 
 // Boundary normalization statistics (page 1, _build_norm_buffers /

@@ -204,6 +204,12 @@ struct EpiResidual {
 // once per call in cs[row][head_dim/2].  q and k go to out[row][q heads | k] in
 // the natural layout; the values go transposed to vt[b][d][vt_ld] (column
 // vt_pos(s)), the layout attention reads them in.
+// Prefix pass (desc != nullptr; page 1, _compute_layer_prefix_only returns the
+// post-RoPE k and v for the cache): S is the padded prefix length, the rotated
+// k head and the values are also stored to the cache desc->kv_out at element
+// offsets k_off / v_off ([B][S][head_dim] blocks, so cache row = GEMM row),
+// and the transposed values of padded rows (s >= valid_len[b]) are zero, so
+// that a masked key's value is exactly zero when attention weighs it by 0.
 template <typename T>
 struct EpiQkvRope {
   static constexpr bool kPaired = true, kRowScale = true, kSsq = false;
@@ -215,9 +221,18 @@ struct EpiQkvRope {
   const float2* cs;
   T* vt;
   int vt_ld;
+  const CallDesc* desc = nullptr;  // prefix pass only
+  size_t k_off = 0, v_off = 0;
   __device__ __forceinline__ int jj(int c) const {
     const int w = c % head_dim;
     return (w >> 5) * 16 + (w & 15);
+  }
+  __device__ __forceinline__ bool is_k(int c) const { return desc != nullptr && c >= qk_cols - head_dim; }
+  __device__ __forceinline__ bool pad_row(int b, int s) const {
+    if (desc == nullptr) return false;
+    int v = desc->valid[b];
+    v = v < 0 ? 0 : (v > S ? S : v);
+    return s >= v;
   }
   __device__ __forceinline__ Pre fetch(int row, int c) const {
     if (c >= qk_cols) return float2{0.f, 0.f};
@@ -227,13 +242,25 @@ struct EpiQkvRope {
     if (c < qk_cols) {
       const int half = head_dim >> 1;
       T* o = out + (size_t)row * ldo + (c / head_dim) * head_dim + jj(c);
-      o[0] = from_f32<T>(x1 * cs_.x - x2 * cs_.y);
-      o[half] = from_f32<T>(x2 * cs_.x + x1 * cs_.y);
+      const T r1 = from_f32<T>(x1 * cs_.x - x2 * cs_.y), r2 = from_f32<T>(x2 * cs_.x + x1 * cs_.y);
+      o[0] = r1;
+      o[half] = r2;
+      if (is_k(c)) {
+        T* kc = reinterpret_cast<T*>(desc->kv_out) + k_off + (size_t)row * head_dim + jj(c);
+        kc[0] = r1;
+        kc[half] = r2;
+      }
     } else {
-      const int b = row / S, s = row - b * S;
-      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + vt_pos(s);
-      o[0] = from_f32<T>(x1);
-      o[(size_t)16 * vt_ld] = from_f32<T>(x2);
+      const int b = row / S, s = row - b * S, d = c - qk_cols;
+      const bool pad = pad_row(b, s);
+      T* o = vt + ((size_t)b * head_dim + d) * vt_ld + vt_pos(s);
+      o[0] = from_f32<T>(pad ? 0.f : x1);
+      o[(size_t)16 * vt_ld] = from_f32<T>(pad ? 0.f : x2);
+      if (desc != nullptr) {
+        T* vc = reinterpret_cast<T*>(desc->kv_out) + v_off + (size_t)row * head_dim + d;
+        vc[0] = from_f32<T>(x1);
+        vc[16] = from_f32<T>(x2);
+      }
     }
   }
   struct Pre8 {
@@ -266,14 +293,25 @@ struct EpiQkvRope {
         r2[e] = x2[e] * p.cs[e].x + x1[e] * p.cs[e].y;
       }
       store8(o, r1);
+      if (is_k(c)) {
+        T* kc = reinterpret_cast<T*>(desc->kv_out) + k_off + (size_t)row * head_dim + jj(c);
+        store8(kc, r1);
+        store8(kc + half, r2);
+      }
       store8(o + half, r2);
     } else {
-      const int b = row / S, s = row - b * S;
-      T* o = vt + ((size_t)b * head_dim + (c - qk_cols)) * vt_ld + vt_pos(s);
+      const int b = row / S, s = row - b * S, d = c - qk_cols;
+      const bool pad = pad_row(b, s);
+      T* o = vt + ((size_t)b * head_dim + d) * vt_ld + vt_pos(s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        o[(size_t)e * vt_ld] = from_f32<T>(x1[e]);
-        o[(size_t)(16 + e) * vt_ld] = from_f32<T>(x2[e]);
+        o[(size_t)e * vt_ld] = from_f32<T>(pad ? 0.f : x1[e]);
+        o[(size_t)(16 + e) * vt_ld] = from_f32<T>(pad ? 0.f : x2[e]);
+      }
+      if (desc != nullptr) {
+        T* vc = reinterpret_cast<T*>(desc->kv_out) + v_off + (size_t)row * head_dim + d;
+        store8(vc, x1);
+        store8(vc + 16, x2);
       }
     }
   }

@@ -167,6 +167,12 @@ struct pi0x_expert {
   }
 };
 
+// The prefix-pass handle: the same core (decoder layers, workspaces, graphs)
+// without an action head.
+struct pi0x_prefix_model {
+  pi0x_expert core;
+};
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -394,31 +400,35 @@ inline int attn_splits(int B, int tiles, int nblk) {
   return std::max(sp, 1);
 }
 
+// prefill: the prefix pass, whose L prefix tokens are the queries and whose
+// keys are the layer's own (cache + the single-layer V^T buffer vtp).
 template <typename T, int DH>
-pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal) {
+pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal, int prefill) {
   constexpr int KB = AttnCfg<T>::KB;
   const int Lp = prefix_pad(L);
+  const int S = prefill ? L : h->S;
   AttnArgs a;
   a.qk = h->qk;
   a.ldqk = h->qd + DH;
   a.col_k = h->qd;
   a.desc = h->desc;
   a.kv_k_off = ((size_t)layer * 2 + 0) * B * L * DH;
-  a.vtp = reinterpret_cast<const T*>(h->vtp) + (size_t)layer * B * DH * Lp;
+  a.vtp = reinterpret_cast<const T*>(h->vtp) + (prefill ? 0 : (size_t)layer * B * DH * Lp);
   a.Lp = Lp;
-  a.vts = h->vts;
-  a.Sp = h->Sp;
+  a.vts = prefill ? nullptr : h->vts;
+  a.Sp = prefill ? 0 : h->Sp;
   a.B = B;
   a.L = L;
-  a.S = h->S;
+  a.S = S;
   a.nh = h->nh;
   a.out = h->o;
   a.ldo = h->qd;
   a.scale = 1.0f / std::sqrt((float)DH);
   a.causal = causal;
-  const int nq = h->nh * h->S;
+  a.prefill = prefill;
+  const int nq = h->nh * S;
   const int tiles = (nq + kAttnQueries - 1) / kAttnQueries;
-  const int nblk = (L + KB - 1) / KB + (h->S + KB - 1) / KB;
+  const int nblk = (L + KB - 1) / KB + (prefill ? 0 : (h->S + KB - 1) / KB);
   a.splits = attn_splits(B, tiles, nblk);
   a.tiles = tiles;
   a.partial = h->attn_partial;
@@ -452,12 +462,12 @@ pi0x_status allow_attn_smem(int dh) {
 }
 
 template <typename T>
-pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal) {
+pi0x_status launch_attn(pi0x_expert* h, hipStream_t s, int B, int L, int layer, int causal, int prefill = 0) {
   switch (h->dh) {
-    case 32: return launch_attn_dh<T, 32>(h, s, B, L, layer, causal);
-    case 64: return launch_attn_dh<T, 64>(h, s, B, L, layer, causal);
-    case 128: return launch_attn_dh<T, 128>(h, s, B, L, layer, causal);
-    case 256: return launch_attn_dh<T, 256>(h, s, B, L, layer, causal);
+    case 32: return launch_attn_dh<T, 32>(h, s, B, L, layer, causal, prefill);
+    case 64: return launch_attn_dh<T, 64>(h, s, B, L, layer, causal, prefill);
+    case 128: return launch_attn_dh<T, 128>(h, s, B, L, layer, causal, prefill);
+    case 256: return launch_attn_dh<T, 256>(h, s, B, L, layer, causal, prefill);
   }
   return fail(PI0X_ERR_SHAPE, "unsupported head_dim");
 }
@@ -519,7 +529,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
   PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, state_tok());
   auto rope_rows = [&]() -> pi0x_status {
     hipLaunchKernelGGL(rope_rows_kernel, dim3(R), dim3(128), 0, s, h->desc, S, L, h->dh / 2, h->rope_cos, h->rope_sin,
-                       h->rope_cs);
+                       h->rope_cs, 1);
     PI0X_HIP(hipGetLastError());
     return PI0X_OK;
   };
@@ -560,11 +570,10 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
   return PI0X_OK;
 }
 
-pi0x_status run(pi0x_expert* h, int B, int L, int N, const LoopOpts& lo, hipStream_t stream) {
-  const Key key{B, L, N, N > 0 ? 0 : 1, lo.bits()};
-  auto launch_eager = [&](hipStream_t s) -> pi0x_status {
-    return h->bf16() ? enqueue<bf16>(h, s, B, L, N, lo) : enqueue<float>(h, s, B, L, N, lo);
-  };
+// Replays the graph recorded for key (recording it on first use), or runs
+// eagerly when graphs are off or kernel timing is on.
+template <class F>
+pi0x_status run_graph(pi0x_expert* h, const Key& key, F launch_eager, hipStream_t stream) {
   if (!h->cfg.use_graphs || h->timing) return launch_eager(stream);
   auto it = h->graphs.find(key);
   if (it == h->graphs.end()) {
@@ -596,6 +605,68 @@ pi0x_status run(pi0x_expert* h, int B, int L, int N, const LoopOpts& lo, hipStre
   }
   PI0X_HIP(hipGraphLaunch(it->second.second, stream));
   return PI0X_OK;
+}
+
+pi0x_status run(pi0x_expert* h, int B, int L, int N, const LoopOpts& lo, hipStream_t stream) {
+  auto launch_eager = [&](hipStream_t s) -> pi0x_status {
+    return h->bf16() ? enqueue<bf16>(h, s, B, L, N, lo) : enqueue<float>(h, s, B, L, N, lo);
+  };
+  return run_graph(h, Key{B, L, N, N > 0 ? 0 : 1, lo.bits()}, launch_eager, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The prefix pass (page 1: the prefix-only branch of
+// PaliGemmaWithExpertModel.forward, _compute_layer_prefix_only per layer, as
+// sample_actions runs it) on a handle that holds only decoder layers.  Per
+// layer: q/k/v + RoPE (the epilogue also stores the post-RoPE k and the v to
+// the caller's cache), attention of the prefix tokens over the real ones,
+// o_proj + residual, gate/up + GeGLU, down + residual -- the same kernels as
+// the expert.  The last layer stops after its k/v: its attention output and
+// MLP only feed the prefix hidden states, which the sampler discards (and so
+// does the final norm, which is not applied).
+// ---------------------------------------------------------------------------
+template <typename T>
+pi0x_status enqueue_prefix(pi0x_expert* h, hipStream_t s, int B, int L) {
+  const int W = h->W, R = B * L, dh = h->dh, Lp = prefix_pad(L);
+  const bool bf = h->bf16();
+  T* hb = bf ? reinterpret_cast<T*>(h->hb) : nullptr;
+  const void* hA = bf ? h->hb : (const void*)h->hbuf;
+  const int G = producer_group(bf, R);
+  const int np = W / G;
+  const NormIn nin{h->ssq, np};
+  auto first = [&]() -> pi0x_status {
+    hipLaunchKernelGGL((prefix_in_kernel<T>), dim3(R), dim3(256), 0, s, h->desc, W, h->hbuf, hb, h->ssq, G);
+    PI0X_HIP(hipGetLastError());
+    hipLaunchKernelGGL(rope_rows_kernel, dim3(R), dim3(128), 0, s, h->desc, L, L, dh / 2, h->rope_cos, h->rope_sin,
+                       h->rope_cs, 0);
+    PI0X_HIP(hipGetLastError());
+    return PI0X_OK;
+  };
+  PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED, first());
+  for (int l = 0; l < h->D; ++l) {
+    const Layer& ly = h->layers[l];
+    EpiQkvRope<T> qe{(T*)h->qk, h->qd + dh, h->qd + dh, dh, L, h->rope_cs, (T*)h->vtp, Lp};
+    qe.desc = h->desc;
+    qe.k_off = ((size_t)l * 2 + 0) * R * dh;
+    qe.v_off = ((size_t)l * 2 + 1) * R * dh;
+    PI0X_TIMED(PI0X_KERNEL_QKV_ROPE, (launch_gemm<T>(h, s, hA, W, ly.wqkv, R, h->nqkv, W, qe, nin)));
+    if (l == h->D - 1) break;
+    PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l, 0, 1));
+    PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
+                                                   EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+    PI0X_TIMED(PI0X_KERNEL_GATE_UP,
+               (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin)));
+    PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M,
+                                                 EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+  }
+  return PI0X_OK;
+}
+
+pi0x_status run_prefix(pi0x_expert* h, int B, int L, hipStream_t stream) {
+  auto launch_eager = [&](hipStream_t s) -> pi0x_status {
+    return h->bf16() ? enqueue_prefix<bf16>(h, s, B, L) : enqueue_prefix<float>(h, s, B, L);
+  };
+  return run_graph(h, Key{B, L, 0, 2, 0}, launch_eager, stream);
 }
 
 pi0x_status check_config(const pi0x_config* c) {
@@ -634,8 +705,9 @@ void put<float>(std::vector<float>& dst, size_t i, float v) { dst[i] = v; }
 template <>
 void put<uint16_t>(std::vector<uint16_t>& dst, size_t i, float v) { dst[i] = host_bf16(v); }
 
+// head == false: a prefix-pass blob (decoder layers only).
 template <typename E>
-pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
+pi0x_status upload_weights(pi0x_expert* h, const float* blob, bool head) {
   const int W = h->W, M = h->M, qd = h->qd, dh = h->dh, half = dh / 2;
   const size_t layer_sz = (size_t)W + (size_t)qd * W + 2 * (size_t)dh * W + (size_t)W * qd + W + 3 * (size_t)M * W;
   auto up = [&](void** dst, const std::vector<E>& v) -> pi0x_status {
@@ -705,6 +777,7 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob) {
       PI0X_TRY(up(&ly.wdown, v));
     }
   }
+  if (!head) return PI0X_OK;
   const float* p = blob + (size_t)h->D * layer_sz;
   const float* final_norm = p;
   const float* ws = final_norm + W;
@@ -790,8 +863,8 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
   h->Lpmax = prefix_pad(h->Lmax);
   h->Sp = round_up(h->S, 64);
   const float* blob = static_cast<const float*>(weights_host);
-  if (h->bf16()) PI0X_TRY(upload_weights<uint16_t>(h, blob));
-  else PI0X_TRY(upload_weights<float>(h, blob));
+  if (h->bf16()) PI0X_TRY(upload_weights<uint16_t>(h, blob, true));
+  else PI0X_TRY(upload_weights<float>(h, blob, true));
 
   const size_t R = (size_t)h->Bmax * h->S, AR = (size_t)h->Bmax * h->H, e = h->esz;
   PI0X_TRY(h->allocT(&h->hbuf, R * h->W * 4));
@@ -830,6 +903,86 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
   PI0X_TRY(h->allocT(&h->rope_cos, (size_t)P * (h->dh / 2) * 4));
   PI0X_TRY(h->allocT(&h->rope_sin, (size_t)P * (h->dh / 2) * 4));
   PI0X_TRY(h->allocT(&h->rope_cs, (size_t)h->Bmax * h->S * (h->dh / 2) * sizeof(float2)));
+  const int n = P * (h->dh / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, P, h->dh, (double)cfg->rope_theta,
+                     h->rope_cos, h->rope_sin);
+  PI0X_HIP(hipGetLastError());
+  PI0X_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  if (h->bf16()) PI0X_TRY(allow_tile_smem_all());
+  if (h->bf16()) PI0X_TRY(allow_attn_smem<bf16>(h->dh));
+  else PI0X_TRY(allow_attn_smem<float>(h->dh));
+  PI0X_HIP(hipDeviceSynchronize());
+  return PI0X_OK;
+}
+
+// Prefix-pass handle: the decoder layers and the workspaces of
+// max_batch x max_prefix_len rows.
+constexpr long kMaxPrefixRows = 1L << 16;
+
+pi0x_status check_prefix_config(const pi0x_config* c) {
+  if (!c) return fail(PI0X_ERR_INVALID_ARG, "config is NULL");
+  pi0x_config k = *c;  // the action-head fields do not apply to the prefix pass
+  k.action_horizon = 1;
+  k.action_dim = 1;
+  k.state_dim = 1;
+  k.max_steps = 1;
+  k.time_min_period = k.time_max_period = 1.f;
+  PI0X_TRY(check_config(&k));
+  if (c->max_prefix_len < 1) return fail(PI0X_ERR_INVALID_ARG, "max_prefix_len must be >= 1");
+  if ((long)c->max_batch * c->max_prefix_len > kMaxPrefixRows)
+    return fail(PI0X_ERR_CAPACITY, "max_batch * max_prefix_len exceeds 65536 rows");
+  return PI0X_OK;
+}
+
+size_t prefix_weight_count(const pi0x_config* c) {
+  const size_t W = c->width, M = c->mlp_dim, qd = (size_t)c->num_heads * c->head_dim,
+               kd = (size_t)c->num_kv_heads * c->head_dim;
+  return (W + qd * W + 2 * kd * W + W * qd + W + 3 * M * W) * c->depth;
+}
+
+pi0x_status create_prefix_impl(const pi0x_config* cfg, const void* weights_host, pi0x_expert* h) {
+  h->cfg = *cfg;
+  PI0X_HIP(hipGetDevice(&h->device));
+  h->esz = cfg->dtype == PI0X_BF16 ? 2 : 4;
+  h->W = cfg->width; h->D = cfg->depth; h->M = cfg->mlp_dim; h->nh = cfg->num_heads; h->dh = cfg->head_dim;
+  h->H = h->A = h->Sd = 0;
+  h->qd = h->nh * h->dh; h->nqkv = h->qd + 2 * h->dh; h->Bmax = cfg->max_batch; h->Lmax = cfg->max_prefix_len;
+  h->Lpmax = prefix_pad(h->Lmax);
+  h->S = h->Lmax;
+  h->Sp = 0;
+  const float* blob = static_cast<const float*>(weights_host);
+  if (h->bf16()) PI0X_TRY(upload_weights<uint16_t>(h, blob, false));
+  else PI0X_TRY(upload_weights<float>(h, blob, false));
+
+  const size_t R = (size_t)h->Bmax * h->Lmax, e = h->esz;
+  PI0X_TRY(h->allocT(&h->hbuf, R * h->W * 4));
+  if (h->bf16()) PI0X_TRY(h->alloc(&h->hb, R * h->W * e));
+  PI0X_TRY(h->allocT(&h->ssq, R * (h->W / 16) * 4));
+  PI0X_TRY(h->alloc(&h->qk, R * (h->qd + h->dh) * e));
+  // one layer's transposed values; never holds a non-finite value the kernels
+  // did not compute, so masked keys weigh exactly zero
+  const size_t vt_bytes = (size_t)h->Bmax * h->dh * h->Lpmax * e;
+  PI0X_TRY(h->alloc(&h->vtp, vt_bytes));
+  PI0X_HIP(hipMemset(h->vtp, 0, vt_bytes));
+  PI0X_TRY(h->alloc(&h->o, R * h->qd * e));
+  PI0X_TRY(h->alloc(&h->gbuf, R * h->M * e));
+  if (h->bf16()) {
+    const int shapes[][2] = {{h->W, h->nqkv}, {h->qd, h->W}, {h->W, 2 * h->M}, {h->M, h->W}};
+    for (const auto& kn : shapes) h->stream_partial_n = std::max(h->stream_partial_n, stream_partial_floats(kn[0], kn[1]));
+    PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
+  }
+  PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
+  if (!h->bf16()) {
+    PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
+    PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
+    PI0X_HIP(hipMemset(h->gemm_counters, 0, (size_t)kCounters * 4));
+  }
+  PI0X_TRY(h->allocT(&h->desc, sizeof(CallDesc)));
+  PI0X_HIP(hipMemset(h->desc, 0, sizeof(CallDesc)));
+  const int P = h->Lmax + 1;
+  PI0X_TRY(h->allocT(&h->rope_cos, (size_t)P * (h->dh / 2) * 4));
+  PI0X_TRY(h->allocT(&h->rope_sin, (size_t)P * (h->dh / 2) * 4));
+  PI0X_TRY(h->allocT(&h->rope_cs, R * (h->dh / 2) * sizeof(float2)));
   const int n = P * (h->dh / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, P, h->dh, (double)cfg->rope_theta,
                      h->rope_cos, h->rope_sin);
@@ -1017,6 +1170,88 @@ void pi0x_expert_destroy(pi0x_expert* h) {
 }
 
 const char* pi0x_last_error(void) { return g_err.c_str(); }
+
+void pi0x_prefix_config_default(pi0x_config* c) {
+  if (!c) return;
+  pi0x_config_default(c);
+  c->width = 2048;
+  c->depth = 18;
+  c->mlp_dim = 16384;
+  c->num_heads = 8;
+  c->num_kv_heads = 1;
+  c->head_dim = 256;
+  c->max_batch = 1;
+  c->max_prefix_len = 1024;
+}
+
+size_t pi0x_prefix_weight_count(const pi0x_config* cfg) {
+  if (!cfg || cfg->width <= 0 || cfg->depth <= 0 || cfg->mlp_dim <= 0 || cfg->num_heads <= 0 ||
+      cfg->num_kv_heads <= 0 || cfg->head_dim <= 0)
+    return 0;
+  return prefix_weight_count(cfg);
+}
+
+pi0x_status pi0x_prefix_create(const pi0x_config* cfg, const void* weights_host, size_t weights_bytes,
+                               pi0x_prefix_model** out) {
+  if (!out) return fail(PI0X_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  PI0X_TRY(check_prefix_config(cfg));
+  if (!weights_host) return fail(PI0X_ERR_INVALID_ARG, "weights_host is NULL");
+  const size_t n = prefix_weight_count(cfg);
+  if (weights_bytes != n * sizeof(float))
+    return fail(PI0X_ERR_SHAPE, "weights_bytes is " + std::to_string(weights_bytes) + ", expected " +
+                                    std::to_string(n * sizeof(float)));
+  pi0x_prefix_model* p = new (std::nothrow) pi0x_prefix_model();
+  if (!p) return fail(PI0X_ERR_OOM, "host allocation failed");
+  pi0x_status st = create_prefix_impl(cfg, weights_host, &p->core);
+  if (st != PI0X_OK) {
+    std::string msg = g_err;
+    destroy_impl(&p->core);
+    delete p;
+    g_err = msg;
+    return st;
+  }
+  *out = p;
+  return PI0X_OK;
+}
+
+pi0x_status pi0x_prefill(pi0x_prefix_model* p, int32_t batch, int32_t prefix_len, const void* prefix_embeddings,
+                         const int32_t* prefix_valid_len, void* prefix_kv_out, hipStream_t stream) {
+  if (!p) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  pi0x_expert* h = &p->core;
+  if (batch < 1) return fail(PI0X_ERR_INVALID_ARG, "batch must be >= 1");
+  if (prefix_len < 0) return fail(PI0X_ERR_INVALID_ARG, "prefix_len must be >= 0");
+  if (batch > h->Bmax) return fail(PI0X_ERR_CAPACITY, "batch exceeds max_batch");
+  if (prefix_len > h->Lmax) return fail(PI0X_ERR_CAPACITY, "prefix_len exceeds max_prefix_len");
+  if (!prefix_embeddings || !prefix_valid_len || !prefix_kv_out)
+    return fail(PI0X_ERR_INVALID_ARG, "a device pointer argument is NULL");
+  if (reinterpret_cast<uintptr_t>(prefix_kv_out) % 16 != 0)
+    return fail(PI0X_ERR_INVALID_ARG, "prefix_kv_out must be 16-byte aligned");
+  int dev = -1;
+  PI0X_HIP(hipGetDevice(&dev));
+  if (dev != h->device) return fail(PI0X_ERR_INVALID_ARG, "the current HIP device is not the handle's device");
+  if (prefix_len == 0) return PI0X_OK;
+  hipLaunchKernelGGL(set_prefix_desc_kernel, dim3(1), dim3(1), 0, stream, h->desc, prefix_embeddings,
+                     prefix_valid_len, prefix_kv_out);
+  PI0X_HIP(hipGetLastError());
+  return run_prefix(h, batch, prefix_len, stream);
+}
+
+void pi0x_prefix_destroy(pi0x_prefix_model* p) {
+  if (!p) return;
+  destroy_impl(&p->core);
+  delete p;
+}
+
+pi0x_status pi0x_prefix_set_timing(pi0x_prefix_model* p, int32_t enable) {
+  if (!p) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  return pi0x_set_timing(&p->core, enable);
+}
+
+pi0x_status pi0x_prefix_read_timing(pi0x_prefix_model* p, double* total_ms, int64_t* launches) {
+  if (!p) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  return pi0x_read_timing(&p->core, total_ms, launches);
+}
 
 pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable) {
   if (!h) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");

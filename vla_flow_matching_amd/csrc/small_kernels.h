@@ -20,6 +20,40 @@ __global__ void set_desc_kernel(CallDesc* d, const void* kv, const int32_t* vali
   d->padding = padding;
 }
 
+// Descriptor of a prefix-pass call: the cache it writes is also the key/value
+// source its attention reads (kv).
+__global__ void set_prefix_desc_kernel(CallDesc* d, const void* emb, const int32_t* valid, void* kv_out) {
+  d->emb = emb;
+  d->valid = valid;
+  d->kv = kv_out;
+  d->kv_out = kv_out;
+}
+
+// First hidden rows of the prefix pass: the embeddings [R][W] (model dtype)
+// copied to the float32 residual stream (and its bf16 copy in bf16 mode), with
+// the sum-of-squares partials over groups of G columns (G <= 256, 1024 % G ==
+// 0) that the first layer's input norm consumes.  One block per row.
+template <typename T>
+__global__ __launch_bounds__(256) void prefix_in_kernel(const CallDesc* __restrict__ desc, int W,
+                                                        float* __restrict__ hbuf, T* __restrict__ hb,
+                                                        float* __restrict__ ssq, int G) {
+  const size_t row = blockIdx.x;
+  const T* e = reinterpret_cast<const T*>(desc->emb) + row * W;
+  const int np = W / G, tpg = G / 4;  // threads per column group
+  for (int c0 = threadIdx.x * 4; c0 < W; c0 += 1024) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = to_f32(e[c0 + k]);
+      hbuf[row * W + c0 + k] = v;
+      if (hb) hb[row * W + c0 + k] = e[c0 + k];
+      ss += v * v;
+    }
+    for (int off = 1; off < tpg; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x % tpg) == 0) ssq[row * np + c0 / G] = ss;
+  }
+}
+
 // State token of every sample (page 1, embed_suffix: state_proj(state)),
 // once per call: hs[b][o] = W_s s_b + b_s (float32).  The token depends on
 // neither x nor t.  One block per sample.
@@ -123,14 +157,19 @@ __global__ void time_features_kernel(const CallDesc* __restrict__ desc, int N, i
   }
 }
 
-// (cos, sin) of every suffix row of the call: row b*S + s sits at position
-// valid_len[b] + s (valid_len clamped to [0, L]); cs[row][j] from the tables.
+// (cos, sin) of every row of the call: suffix row b*S + s sits at position
+// valid_len[b] + s (valid_len clamped to [0, L]); with from_valid == 0 (the
+// prefix pass, right padding: positions cumsum(pad) - 1) row s of a sample
+// sits at position s.  cs[row][j] from the tables.
 __global__ __launch_bounds__(128) void rope_rows_kernel(const CallDesc* __restrict__ desc, int S, int L, int half,
                                                         const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-                                                        float2* __restrict__ cs) {
+                                                        float2* __restrict__ cs, int from_valid) {
   const int row = blockIdx.x, b = row / S, s = row - b * S;
-  int v = desc->valid[b];
-  v = v < 0 ? 0 : (v > L ? L : v);
+  int v = 0;
+  if (from_valid) {
+    v = desc->valid[b];
+    v = v < 0 ? 0 : (v > L ? L : v);
+  }
   const size_t p = (size_t)(v + s) * half;
   for (int j = threadIdx.x; j < half; j += 128) cs[(size_t)row * half + j] = float2{cos_t[p + j], sin_t[p + j]};
 }
