@@ -4,7 +4,9 @@ One "step" is one pi0x_denoise call: the whole num_steps-Euler loop over one
 batch of synthetic inputs already resident in device memory, replayed from its
 captured hipGraph.  The default workload is the bf16 pi0 expert at batch 64
 (prefix 816, horizon 50 x 32, 10 Euler steps); the batch-1 latency workload
-is measured in the same run and reported under "b1".
+is measured in the same run and reported under "b1", and the prefix pass that
+produces the K/V cache (the Gemma-2B-shaped PaliGemma language model over an
+816-token prefix at batch 1) under "prefill".
 
 Output: one JSON line with the throughput (action chunks/s), the roofline
 figure of the dominant kernel (per-launch algorithmic bytes or flops over its
@@ -72,6 +74,84 @@ def kernel_unit_counts(shape, batch: int, esz: int, valid: np.ndarray):
         "attention": {"bytes": (batch * vis * 2 * dh + R * (qd + 2 * dh) + R * qd) * esz,
                       "flops": batch * s.num_heads * 4.0 * dh * (s.horizon * (vis + s.suffix_len) + vis + 1)},
     }
+
+
+def prefill_counts(shape, batch: int, valid: np.ndarray, L: int, esz: int):
+    """Algorithmic bytes and flops of one prefix pass, counted for what the
+    cache needs: every layer in full except the last, which only needs its
+    q/k/v projection (its attention output and MLP feed the discarded prefix
+    output); real tokens only, real keys only; weights once, embeddings in and
+    the cache out.  Norm weights are not counted."""
+    s = shape
+    W, M, qd, kd, dh = s.width, s.mlp_dim, s.num_heads * s.head_dim, s.num_kv_heads * s.head_dim, s.head_dim
+    qkv = W * (qd + 2 * kd)
+    full = qkv + qd * W + 3 * M * W
+    params = (s.depth - 1) * full + qkv
+    rows = float(np.sum(valid))
+    dense = 2.0 * params * rows
+    attn = (s.depth - 1) * s.num_heads * 4.0 * dh * float(np.sum(np.asarray(valid, np.float64) ** 2))
+    nbytes = params * esz + batch * L * W * esz + s.depth * 2 * batch * L * kd * esz
+    unit_rows = batch * L  # rows one launch computes (padding included)
+    units = {"gate_up": {"flops": 2.0 * unit_rows * 2 * M * W, "bytes": (2 * M * W + unit_rows * (W + M)) * esz},
+             "down": {"flops": 2.0 * unit_rows * W * M, "bytes": (W * M + unit_rows * M) * esz + unit_rows * W * 8},
+             "qkv_rope": {"flops": 2.0 * unit_rows * (qd + 2 * kd) * W,
+                          "bytes": ((qd + 2 * kd) * W + unit_rows * (W + qd + 3 * kd)) * esz},
+             "o_proj": {"flops": 2.0 * unit_rows * W * qd, "bytes": (W * qd + unit_rows * qd) * esz + unit_rows * W * 8}}
+    return {"bytes": nbytes, "flops": dense + attn, "units": units}
+
+
+def run_prefill(name: str, steps: int, warmup: int, timing_calls: int = 2):
+    import torch
+    from vla_flow_matching_amd import binding, synth
+
+    w = synth.PREFILL_WORKLOADS[name]
+    s = w.shape
+    esz = 2 if w.dtype == "bf16" else 4
+    blob = synth.make_prefill_weights(s, seed=w.seed, dtype=w.dtype)
+    inputs = synth.make_prefill_inputs(w)
+    cfg = binding.make_config(s, w.dtype, max_batch=w.batch, max_prefix_len=w.prefix_len)
+    pm = binding.PrefixModel(cfg, blob)
+    del blob
+    d = binding.prefill_device_inputs(inputs, w.dtype)
+    kv = torch.empty((s.depth, 2, w.batch, w.prefix_len, s.head_dim), dtype=d["embeddings"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pm.prefill(d["embeddings"], d["valid_len"], out=kv)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    pm.set_timing(True)
+    for _ in range(timing_calls):
+        call()
+    timing = pm.read_timing()
+    pm.set_timing(False)
+    pm.close()
+    valid = inputs["valid_len"]
+    c = prefill_counts(s, w.batch, valid, w.prefix_len, esz)
+    kern = {k: {"avg_us": 1e3 * tot / n, "launches_per_call": n // timing_calls} for k, (tot, n) in timing.items() if n}
+    dom = max((k for k in kern if k in c["units"]), key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_call"])
+    u = c["units"][dom]
+    peak = MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS
+    ach = u["flops"] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+    sec = ms * 1e-3
+    return {"workload": w.name, "batch": w.batch, "prefix_len": w.prefix_len, "real_tokens": int(np.sum(valid)),
+            "ms_per_call": ms, "prefixes_per_s": w.batch / sec,
+            "whole_pass": {"achieved_TFLOPs": c["flops"] / sec / 1e12, "mfma_frac": c["flops"] / sec / 1e12 / peak,
+                           "flops_per_call": c["flops"], "bytes_per_call": c["bytes"],
+                           "achieved_GBps": c["bytes"] / sec / 1e9},
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                         "frac": ach / peak, "traffic": None,
+                         "per_launch": {"flops": u["flops"], "bytes": u["bytes"], "avg_us": kern[dom]["avg_us"]}},
+            "kernels": kern}
 
 
 def csrc_digest() -> str:
@@ -215,6 +295,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pi0_bf16_b64")
     ap.add_argument("--b1-workload", default="pi0_bf16_b1", help="secondary latency workload ('' to skip)")
+    ap.add_argument("--prefill-workload", default="paligemma_bf16_b1",
+                    help="prefix-pass workload reported under 'prefill' ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--latency-calls", type=int, default=100,
                     help="calls timed one by one for the latency median / p10 / p90 (0 to skip)")
@@ -254,6 +336,8 @@ def main():
         line["b1"] = {"workload": r["workload"].name, "chunks_per_s": r["value"], "latency_ms": r["ms"],
                       "latency": r["latency"], "roofline": r["roofline"], "whole_loop": r["whole_loop"],
                       "kernels": r["kernels"]}
+    if args.prefill_workload:
+        line["prefill"] = run_prefill(args.prefill_workload, max(args.steps // 2, 5), args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, main_res["inputs"])
     print(json.dumps(line), flush=True)
