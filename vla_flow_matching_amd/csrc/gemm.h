@@ -617,6 +617,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, Epi epi) {
 // owns a contiguous run of tiles -- and tiles run in groups of group_m row
 // tiles by all column tiles, so the blocks resident on one XCD share their A
 // row panels and W column panels in that XCD's L2.
+//
+// K split (g.splits > 1, for grids with fewer tiles than CUs): unit u of the
+// T * splits units is K range u % splits of tile u / splits, and the block
+// stores its raw float32 tile to g.partial[split][row][col]; gemm_reduce_kernel
+// then adds the splits in order and runs the epilogue.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int ST, int NWM = 2, int NWN = 2>
 constexpr size_t tile_smem_bytes() {
@@ -652,10 +657,12 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
   bf16* ring = reinterpret_cast<bf16*>(smem_raw);
   __shared__ float s_inv[BM];
 
-  // tile of this block
-  const int T = tiles_m * tiles_n, per_xcd = (T + 7) / 8;
-  const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (t >= T) return;
+  // tile (and K range) of this block
+  const int S = g.splits;
+  const int T = tiles_m * tiles_n, U = T * S, per_xcd = (U + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (u >= U) return;
+  const int t = u / S, split = u - t * S;
   const int gsize = group_m * tiles_n, grp = t / gsize, first_m = grp * group_m;
   const int gm = min(tiles_m - first_m, group_m), within = t - grp * gsize;
   const int m_tile = first_m + within % gm, n_tile = within / gm;
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
   const int m0 = m_tile * BM, n0 = n_tile * BN;
-  const int KI = g.K / BK;
+  const int KI = g.K / BK / S, kbase = split * KI * BK;  // this block's K slices
   const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
 
@@ -673,13 +680,13 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
     const int slot = (wave * AJ + j) * 64 + lane, row = slot / CPR, c = (slot % CPR) ^ ((row / RPS) % CPR);
-    asrc[j] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + c * 8;
+    asrc[j] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + kbase + c * 8;
   }
   const bf16* bsrc[BJ];
 #pragma unroll
   for (int j = 0; j < BJ; ++j) {
     const int slot = (wave * BJ + j) * 64 + lane, row = slot / CPR, c = (slot % CPR) ^ ((row / RPS) % CPR);
-    bsrc[j] = W + (size_t)(n0 + row) * g.ldw + c * 8;
+    bsrc[j] = W + (size_t)(n0 + row) * g.ldw + kbase + c * 8;
   }
   auto issue = [&](int kt) {
     bf16* sa = ring + (kt % ST) * STAGE;
@@ -759,6 +766,24 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
         for (int e = 0; e < 4; ++e)
           strip[(ii * 16 + (lane >> 4) * 4 + e) * ELD + j * 16 + (lane & 15)] = acc[2 * i + ii][j][e];
     wave_lds_fence();
+    if (S > 1) {
+      // K split: the raw partial (row scale and epilogue come after the sum)
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int row = mb + i * 32 + p * RPP + rin;
+        if (row >= g.M) continue;
+        float* dst = g.partial + ((size_t)split * g.M + row) * g.N + nb + c;
+        float v[8];
+        load8f(strip + (p * RPP + rin) * ELD + c, v);
+        store8(dst, v);
+        if constexpr (Epi::kPaired) {
+          load8f(strip + (p * RPP + rin) * ELD + c + 16, v);
+          store8(dst + 16, v);
+        }
+      }
+      wave_lds_fence();
+      continue;
+    }
     typename Epi::Pre8 pre[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {

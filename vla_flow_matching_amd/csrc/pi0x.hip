@@ -67,6 +67,10 @@ pi0x_status fail(pi0x_status s, const std::string& msg) {
 
 constexpr int kMaxGraphs = 32;
 constexpr size_t kGemmPartialFloats = (size_t)16 << 20;  // split-K partial tiles (float32 path)
+// K-split partials of the bf16 tile GEMM (128x128 tiles): used while
+// splits x tiles <= 512, so splits x rows x N <= 512 x 128 x 128 floats
+// whatever the shape.
+constexpr size_t kSplitPartialFloats = (size_t)512 * 128 * 128;
 // Attention key splits: used while fewer than kAttnSplitMinBlocks 128-query
 // tiles exist; at most kAttnPartialBlocks split blocks per launch.
 constexpr int kAttnSplitMinBlocks = 128;
@@ -133,6 +137,7 @@ struct pi0x_expert {
   float* stream_partial = nullptr;  // K-split partial tiles of the M <= 64 bf16 GEMMs
   size_t stream_partial_n = 0;
   float* attn_partial = nullptr;  // split attention states [blocks][2 + head_dim/4][512]
+  float* split_partial = nullptr;  // K-split partial tiles of the bf16 tile GEMM (prefix pass)
   unsigned* gemm_counters = nullptr;
   CallDesc* desc = nullptr;
   NormDev* norm = nullptr;  // boundary normalization statistics (all modes 0 at create)
@@ -292,7 +297,7 @@ template <int BN, int ST, class Epi>
 pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
   constexpr int BM = 128, BK = 64;
   const int tm = (g.M + BM - 1) / BM, tn = g.N / BN;
-  const int blocks = 8 * ((tm * tn + 7) / 8);
+  const int blocks = 8 * ((tm * tn * g.splits + 7) / 8);
   constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST>();
   gemm_tile_kernel<BM, BN, BK, ST, 2, 2, Epi><<<dim3(blocks), dim3(256), smem, s>>>(g, epi, tm, tn, 8);
   PI0X_HIP(hipGetLastError());
@@ -304,6 +309,26 @@ pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
   if (g.N > 4096 && g.N % 128 == 0 && !Epi::kSsq) return launch_gemm_tile_cfg<128, 2>(s, g, epi);
   if (g.K >= 2048) return launch_gemm_tile_cfg<64, 3>(s, g, epi);
   return launch_gemm_tile_cfg<64, 2>(s, g, epi);
+}
+
+// The 128x128 tile GEMM split over K (g.K / 64 divisible by splits, N a
+// multiple of 128): raw float32 partial tiles, then gemm_reduce_kernel adds
+// them in split order and runs the epilogue (residual producers then write
+// sum-of-squares partials per kStreamGroup columns).  For long-K projections
+// with too few tiles to fill the chip: more tiles in flight per CU hide the
+// latency of the weight stream.
+template <class Epi>
+pi0x_status launch_gemm_tile_split(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi& epi, int splits) {
+  if ((g.K / 64) % splits != 0 || g.N % 128 != 0) return fail(PI0X_ERR_SHAPE, "unsupported K-split GEMM shape");
+  if (!h->split_partial || (size_t)splits * g.M * g.N > kSplitPartialFloats)
+    return fail(PI0X_ERR_SHAPE, "K-split partials exceed the workspace");
+  g.splits = splits;
+  g.partial = h->split_partial;
+  PI0X_TRY((launch_gemm_tile_cfg<128, 2>(s, g, epi)));
+  const int cols = Epi::kPaired ? 512 : kStreamGroup;
+  gemm_reduce_kernel<Epi><<<dim3((g.N + cols - 1) / cols, g.M), dim3(64), 0, s>>>(g, epi);
+  PI0X_HIP(hipGetLastError());
+  return PI0X_OK;
 }
 
 template <int NW, int TN, class Epi>
@@ -631,9 +656,23 @@ pi0x_status enqueue_prefix(pi0x_expert* h, hipStream_t s, int B, int L) {
   const bool bf = h->bf16();
   T* hb = bf ? reinterpret_cast<T*>(h->hb) : nullptr;
   const void* hA = bf ? h->hb : (const void*)h->hbuf;
-  const int G = producer_group(bf, R);
+  // down (the long-K residual producer): when its tiles cannot fill the chip
+  // (816 rows: 7 x 16 tiles of 128x128) it is split over K (up to 4 ways, at
+  // most 512 blocks) and reduced by gemm_reduce_kernel, whose sum-of-squares
+  // groups are kStreamGroup columns; the embedding copy then uses the same
+  // groups, since both feed the next q/k/v projection.  o_proj keeps the
+  // unsplit kernel's groups for gate/up.
+  const int tiles_down = ((R + 127) / 128) * (W / 128);
+  int dsplit = 1;
+  if (bf && R > kSmallRows && tiles_down < 256 && W % 128 == 0) {
+    dsplit = std::max(1, std::min(4, 512 / tiles_down));
+    while (dsplit > 1 && (h->M / 64) % dsplit != 0) --dsplit;
+  }
+  const int G = dsplit > 1 ? kStreamGroup : producer_group(bf, R);  // embedding copy and down
   const int np = W / G;
   const NormIn nin{h->ssq, np};
+  const int np_post = W / producer_group(bf, R);  // o_proj
+  const NormIn nin_post{h->ssq, np_post};
   auto first = [&]() -> pi0x_status {
     hipLaunchKernelGGL((prefix_in_kernel<T>), dim3(R), dim3(256), 0, s, h->desc, W, h->hbuf, hb, h->ssq, G);
     PI0X_HIP(hipGetLastError());
@@ -653,11 +692,19 @@ pi0x_status enqueue_prefix(pi0x_expert* h, hipStream_t s, int B, int L) {
     if (l == h->D - 1) break;
     PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l, 0, 1));
     PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
-                                                   EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+                                                   EpiResidual<T>{h->hbuf, hb, W, h->ssq, np_post})));
     PI0X_TIMED(PI0X_KERNEL_GATE_UP,
-               (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin)));
-    PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M,
-                                                 EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+               (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin_post)));
+    const EpiResidual<T> down_epi{h->hbuf, hb, W, h->ssq, np};
+    if (dsplit > 1) {
+      if constexpr (sizeof(T) == 2) {
+        PI0X_TIMED(PI0X_KERNEL_DOWN,
+                   launch_gemm_tile_split(h, s, make_args(h, h->gbuf, h->M, ly.wdown, R, W, h->M, NormIn()),
+                                          down_epi, dsplit));
+      }
+    } else {
+      PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M, down_epi)));
+    }
   }
   return PI0X_OK;
 }
@@ -972,6 +1019,7 @@ pi0x_status create_prefix_impl(const pi0x_config* cfg, const void* weights_host,
     PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
   }
   PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
+  if (h->bf16()) PI0X_TRY(h->allocT(&h->split_partial, kSplitPartialFloats * 4));
   if (!h->bf16()) {
     PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
     PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
