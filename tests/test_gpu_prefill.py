@@ -211,6 +211,26 @@ def test_gemma_2b_two_layers_full_prefix_bf16():
         c.close()
 
 
+def test_gemma_2b_two_layers_batched_ragged_bf16():
+    # full width, batch 4 of a 256-token padded prefix with ragged real lengths:
+    # 1024 GEMM rows (the K-split down projection over 8 row tiles), 4 samples
+    # of attention, NaN in every padded embedding
+    s = dataclasses.replace(synth.GEMMA_2B, depth=2)
+    w = synth.PrefillWorkload("gemma2b_d2_bf16_b4", s, "bf16", 4, 256, seed=17)
+    valid = [256, 200, 131, 40]
+    c = Case(w, norm_std=0.0, valid=valid)
+    try:
+        emb = c.dev["embeddings"].clone()
+        for b, v in enumerate(valid):
+            emb[b, v:] = float("nan")
+        d2 = dict(c.dev)
+        d2["embeddings"] = emb
+        out = c.run(dev=d2)
+        check_close(real_rows(out, valid), real_rows(c.ref(), valid), "bf16", "gemma-2b depth 2, B=4 ragged")
+    finally:
+        c.close()
+
+
 def test_gemma_2b_full_depth_short_prefix_bf16():
     # all 18 layers at full width over an 816-row padded prefix with 48 real
     # tokens (the padded rows run through the same kernels and are never read)
