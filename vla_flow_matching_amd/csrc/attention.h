@@ -38,6 +38,8 @@
 // the same keys run together on one XCD and share them in its L2.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pi0x {
@@ -354,24 +356,46 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
   if (qi >= nq) return;
   const int qs = qi / a.nh, qn = qi - qs * a.nh;
   const float* P = a.partial + ((size_t)b * a.tiles + tile) * a.splits * (QT * NR * NT) + (size_t)t * NR * NT + tid;
-  float mz = -INFINITY;
-#pragma unroll 8
-  for (int z = 0; z < a.splits; ++z) mz = fmaxf(mz, P[(size_t)z * QT * NR * NT]);
-  float l = 0.f;
+  // splits in batches of ZC (4, 8 or 16, the smallest that covers the splits):
+  // every load of a batch is issued before any is used (one memory round trip
+  // per batch), and the running maximum carries over between batches; with
+  // splits <= ZC this is the plain two-pass merge
+  float m = -INFINITY, l = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int z = 0; z < a.splits; ++z) {
-    const float* pz = P + (size_t)z * QT * NR * NT;
-    float v[6];
-    v[0] = pz[0];
-    v[1] = pz[NT];
+  auto merge = [&](auto zc) {
+    constexpr int ZC = decltype(zc)::value;
+    for (int z0 = 0; z0 < a.splits; z0 += ZC) {
+      float vm[ZC], vl[ZC], vo[ZC][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[2 + e] = pz[(2 + d0 * 4 + e) * NT];
-    const float w = (v[0] == -INFINITY) ? 0.f : fexp<T>(v[0] - mz);
-    l += w * v[1];
+      for (int k = 0; k < ZC; ++k) {
+        const float* pz = P + (size_t)min(z0 + k, a.splits - 1) * QT * NR * NT;
+        vm[k] = pz[0];
+        vl[k] = pz[NT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] += w * v[2 + e];
-  }
+        for (int e = 0; e < 4; ++e) vo[k][e] = pz[(2 + d0 * 4 + e) * NT];
+      }
+      float mb = m;
+#pragma unroll
+      for (int k = 0; k < ZC; ++k)
+        if (z0 + k < a.splits) mb = fmaxf(mb, vm[k]);
+      const float s0 = (m == -INFINITY) ? 0.f : fexp<T>(m - mb);
+      l *= s0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= s0;
+#pragma unroll
+      for (int k = 0; k < ZC; ++k) {
+        if (z0 + k >= a.splits) continue;
+        const float w = (vm[k] == -INFINITY) ? 0.f : fexp<T>(vm[k] - mb);
+        l += w * vl[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += w * vo[k][e];
+      }
+      m = mb;
+    }
+  };
+  if (a.splits <= 4) merge(std::integral_constant<int, 4>());
+  else if (a.splits <= 8) merge(std::integral_constant<int, 8>());
+  else merge(std::integral_constant<int, 16>());
   const float inv = l > 0.f ? 1.f / l : 0.f;
   T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.S + qs) * a.ldo + qn * DH;
 #pragma unroll
