@@ -244,3 +244,46 @@ def test_full_bf16_b64_causal_sampled():
             check_close(out[b], ref[i], "bf16", f"pi0 bf16 B=64 causal N=2, sample {b}")
     finally:
         c.close()
+
+
+def test_variants_with_boundary_normalization(tiny):
+    # normalization and the loop variants compose: the state is normalized,
+    # the loop (0 -> 1 grid, x-prediction, causal, padding blend in the
+    # normalized space) runs, the returned chunk is unnormalized
+    s = tiny.w.shape
+    rng = np.random.default_rng(51)
+    sn = {"mode": "min_max", "min": rng.uniform(-2, -1, s.state_dim).astype(np.float32),
+          "max": rng.uniform(1, 2, s.state_dim).astype(np.float32)}
+    an = {"mode": "mean_std", "mean": rng.standard_normal(s.action_dim - 4).astype(np.float32),
+          "std": rng.uniform(0.5, 2.0, s.action_dim - 4).astype(np.float32)}
+    tiny.ex.set_normalization(sn, an)
+    try:
+        out = tiny.run(3, "zero_to_one", True, True, True)
+    finally:
+        tiny.ex.set_normalization(None, None)
+    opts = dict(schedule="zero_to_one", x_prediction=True, causal=True, dof_mask=tiny.mask, padding=tiny.pad)
+    ref = tiny.oracle.denoise_batch(tiny.inputs, 3, state_norm=sn, action_norm=an, options=opts)
+    check_close(out, ref, "fp32", "tiny variants + normalization")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_tiny_fp32_seeded_sweep(case):
+    # seeded random configurations: batch, padded and valid prefix lengths
+    # (including an empty prefix and valid length 0), steps, schedule and
+    # every loop option
+    rng = np.random.default_rng(1000 + case)
+    B = int(rng.integers(1, 6))
+    L = int(rng.choice([0, 1, 17, 40, 64], p=[0.1, 0.1, 0.25, 0.25, 0.3]))
+    valid = rng.integers(0, L + 1, size=B)
+    n = int(rng.integers(1, 5))
+    schedule = str(rng.choice(["pi0", "zero_to_one"]))
+    xp, causal, blend = (bool(v) for v in rng.integers(0, 2, size=3))
+    w = TINY.replace(name=f"tiny_sweep_{case}", batch=B, prefix_len=L, seed=2000 + case)
+    c = Case(w, valid=valid)
+    try:
+        out = c.run(n, schedule, xp, causal, blend)
+        check_close(out, c.ref(n, schedule, xp, causal, blend), "fp32",
+                    f"sweep {case}: B={B} L={L} valid={list(valid)} N={n} {schedule} xpred={xp} causal={causal} "
+                    f"blend={blend}")
+    finally:
+        c.close()

@@ -337,7 +337,7 @@ def device_inputs(inputs: dict, dtype: str, device: str = "cuda"):
     prefix_kv [depth][2][B][L][head_dim] in the model dtype, the rest as given."""
     import torch
     kv = inputs["prefix_kv"]
-    kv = kv.reshape(kv.shape[0], kv.shape[1], kv.shape[2], kv.shape[3], -1)
+    kv = kv.reshape(kv.shape[0], kv.shape[1], kv.shape[2], kv.shape[3], int(np.prod(kv.shape[4:])))
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     return {
         "prefix_kv": torch.from_numpy(np.ascontiguousarray(kv)).to(device=device, dtype=tdt),
