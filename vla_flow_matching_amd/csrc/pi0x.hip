@@ -696,15 +696,15 @@ pi0x_status enqueue_prefix(pi0x_expert* h, hipStream_t s, int B, int L) {
     PI0X_TIMED(PI0X_KERNEL_GATE_UP,
                (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin_post)));
     const EpiResidual<T> down_epi{h->hbuf, hb, W, h->ssq, np};
-    if (dsplit > 1) {
+    auto down = [&]() -> pi0x_status {
       if constexpr (sizeof(T) == 2) {
-        PI0X_TIMED(PI0X_KERNEL_DOWN,
-                   launch_gemm_tile_split(h, s, make_args(h, h->gbuf, h->M, ly.wdown, R, W, h->M, NormIn()),
-                                          down_epi, dsplit));
+        if (dsplit > 1)
+          return launch_gemm_tile_split(h, s, make_args(h, h->gbuf, h->M, ly.wdown, R, W, h->M, NormIn()), down_epi,
+                                        dsplit);
       }
-    } else {
-      PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M, down_epi)));
-    }
+      return launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M, down_epi);
+    };
+    PI0X_TIMED(PI0X_KERNEL_DOWN, down());
   }
   return PI0X_OK;
 }
