@@ -346,6 +346,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pi0_bf16_b64")
     ap.add_argument("--b1-workload", default="pi0_bf16_b1", help="secondary latency workload ('' to skip)")
+    ap.add_argument("--ragged-workload", default="pi0_bf16_b16_ragged",
+                    help="ragged-prefix workload reported under 'ragged' ('' to skip)")
     ap.add_argument("--prefill-workload", default="paligemma_bf16_b1",
                     help="prefix-pass workload reported under 'prefill' ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -389,14 +391,22 @@ def main():
         line["b1"] = {"workload": r["workload"].name, "chunks_per_s": r["value"], "latency_ms": r["ms"],
                       "latency": r["latency"], "roofline": r["roofline"], "whole_loop": r["whole_loop"],
                       "kernels": r["kernels"]}
+    if args.ragged_workload:
+        r = run_workload(args.ragged_workload, max(args.steps, 20), args.warmup, latency_calls=0)
+        rw = r["workload"]
+        line["ragged"] = {"workload": rw.name, "batch": rw.batch, "prefix_len": rw.prefix_len,
+                          "valid_len": [int(v) for v in r["inputs"]["valid_len"]], "num_steps": rw.num_steps,
+                          "chunks_per_s": r["value"], "ms_per_call": r["ms"], "roofline": r["roofline"],
+                          "whole_loop": r["whole_loop"], "kernels": r["kernels"]}
     if args.prefill_workload:
         line["prefill"] = run_prefill(args.prefill_workload, max(args.steps // 2, 5), args.warmup)
     if args.copy_bandwidth:
         cb = copy_bandwidth()
         line["hbm_copy"] = cb
         line["whole_loop"]["hbm_frac_of_copy"] = line["whole_loop"]["achieved_GBps"] / cb["GBps"]
-        if "b1" in line:
-            line["b1"]["whole_loop"]["hbm_frac_of_copy"] = line["b1"]["whole_loop"]["achieved_GBps"] / cb["GBps"]
+        for sub in ("b1", "ragged"):
+            if sub in line:
+                line[sub]["whole_loop"]["hbm_frac_of_copy"] = line[sub]["whole_loop"]["achieved_GBps"] / cb["GBps"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, main_res["inputs"])
     print(json.dumps(line), flush=True)

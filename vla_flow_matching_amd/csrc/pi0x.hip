@@ -529,10 +529,33 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
   // A operand of the norm-consuming projections: the residual stream itself
   // (its bf16 copy in bf16 mode)
   const void* hA = bf ? h->hb : (const void*)h->hbuf;
-  // sum-of-squares partials: one per (row, producer column group)
-  const int G = producer_group(bf, R);
+  // sum-of-squares partials: one per (row, producer column group); every
+  // consumer reads them with its producer's group width
+  const int G = producer_group(bf, R);  // state-token copy, action-row MLP output, o_proj
   const int np = W / G;
   const NormIn nin{h->ssq, np};
+  // down (the longest-K residual producer): when its 128x64 tiles cannot fill
+  // the chip (816 suffix rows at batch 16: 7 x 16 tiles) it runs as 128x128
+  // tiles split over K (up to 8 ways, at most 512 blocks), reduced by
+  // gemm_reduce_kernel, whose groups are kStreamGroup columns; the next
+  // layer's q/k/v and the final projection read those.  o_proj and the
+  // action-row MLP output (K <= 2048) measured no faster split and keep the
+  // unsplit kernels.
+  int dsplit = 1;
+  if (bf && R > kSmallRows && ((R + 127) / 128) * (W / 64) < 256 && W % 128 == 0) {
+    dsplit = std::min(8, 512 / (((R + 127) / 128) * (W / 128)));
+    while (dsplit > 1 && (h->M / 64) % dsplit != 0) --dsplit;
+  }
+  const int np_down = dsplit > 1 ? W / kStreamGroup : np;
+  const NormIn nin_down{h->ssq, np_down};
+  auto down_proj = [&](const Layer& ly) -> pi0x_status {
+    const EpiResidual<T> epi{h->hbuf, hb, W, h->ssq, np_down};
+    if constexpr (sizeof(T) == 2) {
+      if (dsplit > 1)
+        return launch_gemm_tile_split(h, s, make_args(h, h->gbuf, h->M, ly.wdown, R, W, h->M, NormIn()), epi, dsplit);
+    }
+    return launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M, epi);
+  };
 
   auto time_feats = [&]() -> pi0x_status {
     hipLaunchKernelGGL((time_features_kernel<T>), dim3(steps), dim3(256), 0, s, h->desc, N, lo.zero_to_one, W,
@@ -578,19 +601,18 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
                  (launch_gemm<T>(h, s, hA, W, ly.wqkv, R, h->nqkv, W,
                                  EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, h->rope_cs,
                                                (T*)h->vts, h->Sp},
-                                 nin)));
+                                 l == 0 ? nin : nin_down)));
       PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l, lo.causal));
       PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
                                                      EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
       PI0X_TIMED(PI0X_KERNEL_GATE_UP,
                  (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin)));
-      PI0X_TIMED(PI0X_KERNEL_DOWN, (launch_gemm<T>(h, s, h->gbuf, h->M, ly.wdown, R, W, h->M,
-                                                   EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+      PI0X_TIMED(PI0X_KERNEL_DOWN, down_proj(ly));
     }
     const int last = (k == steps - 1);
     const EpiEuler epi{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1,
                        step_dt(k, N, lo.zero_to_one != 0), h->norm, lo.xpred, lo.blend && first};
-    PI0X_TIMED(PI0X_KERNEL_FINAL, (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W, epi, nin)));
+    PI0X_TIMED(PI0X_KERNEL_FINAL, (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W, epi, nin_down)));
   }
   return PI0X_OK;
 }
@@ -934,6 +956,7 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
     PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
   }
   PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
+  if (h->bf16()) PI0X_TRY(h->allocT(&h->split_partial, kSplitPartialFloats * 4));
   if (!h->bf16()) {
     PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
     PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
