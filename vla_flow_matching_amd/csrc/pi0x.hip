@@ -612,7 +612,19 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
     const int last = (k == steps - 1);
     const EpiEuler epi{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1,
                        step_dt(k, N, lo.zero_to_one != 0), h->norm, lo.xpred, lo.blend && first};
-    PI0X_TIMED(PI0X_KERNEL_FINAL, (launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W, epi, nin_down)));
+    // the final projection has Apad (128) columns: beyond batch 1 its few
+    // tiles are split over K (at most 512 blocks) and reduced in split order
+    auto final_proj = [&]() -> pi0x_status {
+      if constexpr (sizeof(T) == 2) {
+        if (R > kSmallRows) {
+          int sp = std::min(8, 512 / (((R + 127) / 128) * (h->Apad / 128)));
+          while (sp > 1 && (W / 64) % sp != 0) --sp;
+          if (sp > 1) return launch_gemm_tile_split(h, s, make_args(h, hA, W, h->w_outp, R, h->Apad, W, nin_down), epi, sp);
+        }
+      }
+      return launch_gemm<T>(h, s, hA, W, h->w_outp, R, h->Apad, W, epi, nin_down);
+    };
+    PI0X_TIMED(PI0X_KERNEL_FINAL, final_proj());
   }
   return PI0X_OK;
 }
