@@ -20,12 +20,19 @@
 // (plus the state token copy), action_time_mlp_out (writes the action rows of
 // the residual stream), per layer [q/k/v + RoPE, attention, o_proj + residual,
 // gate/up + GeGLU, down + residual], and action_out_proj + Euler update (the
-// final norm's 1/rms applied as a row scale).  Once per call: the time
+// final norm's 1/rms applied as a row scale), plus a reduce launch for every
+// projection split over K and a combine launch for attention split over keys
+// (small and mid batches).  Once per call: the time
 // features of every step, the time half of action_time_mlp_in for every step,
-// the transpose of the prefix values and the state tokens.  A call writes a small device descriptor with its pointers and
-// replays the hipGraph recorded for (batch, prefix length, steps, mode); the
-// graph is recorded on first use, so later calls with new buffers or new
-// valid lengths replay it unchanged.
+// the transpose of the prefix values and the state tokens.  A call writes a
+// small device descriptor with its pointers and replays the hipGraph recorded
+// for (batch, prefix length, steps, mode, loop options); the graph is recorded
+// on first use, so later calls with new buffers or new valid lengths replay it
+// unchanged.
+//
+// The prefix pass (pi0x_prefill) runs on a handle of its own that holds only
+// decoder layers; it reuses the same GEMM, attention and epilogue kernels and
+// writes the per-layer K/V cache the denoise loop reads.
 #include "pi0x.h"
 
 #include <cmath>
@@ -523,7 +530,6 @@ template <typename T>
 pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const LoopOpts& lo) {
   const int W = h->W, S = h->S, H = h->H, R = B * S, AR = B * H;
   const int steps = N > 0 ? N : 1;
-  const float eps = h->cfg.rms_eps;
   const bool bf = h->bf16();
   T* hb = bf ? reinterpret_cast<T*>(h->hb) : nullptr;
   // A operand of the norm-consuming projections: the residual stream itself
