@@ -7,10 +7,10 @@
 //  * gemm_kernel      16x16 tiles, bf16 or fp32 operands (fp32 through eight
 //                     v_mfma_f32_16x16x4_f32 per 32-wide K slice): the float32
 //                     path and the fallback for any shape.
-//  * gemm_tile_kernel bf16, v_mfma_f32_16x16x32_bf16, 128x128 block tiles of
-//                     2x2 waves, K slices DMA'd straight into an LDS ring,
-//                     XCD-aware tile order: the compute-bound shapes (more
-//                     than 64 rows, i.e. batch >= 2).
+//  * gemm_tile_kernel bf16, v_mfma_f32_16x16x32_bf16, 128x128 or 128x64
+//                     block tiles of 2x2 waves, K slices DMA'd straight into
+//                     an LDS ring, XCD-aware tile order: the compute-bound
+//                     shapes (more than 64 rows, i.e. batch >= 2).
 //  * gemm_wide_kernel  bf16, M <= 64 (batch 1), every projection but the
 //                     residual producers: one block per 16-32 columns over the
 //                     whole K range, a K chunk's loads in flight at once,
@@ -29,11 +29,14 @@
 // return h_new^2 per element; the kernel sums them over each wave's (or
 // block's) column group and stores one partial per (row, group).
 //
-// Split-K (gemm_kernel only): the K range is divided over gridDim.z; each
-// block writes its partial tile and the last block to arrive adds the shares
-// in split order and runs the epilogue.  The hand-off needs device-scope
-// fences, which cost tens of microseconds on this part, so the bf16 kernels
-// never split K.
+// Split-K.  gemm_kernel (float32 path): the K range is divided over
+// gridDim.z; each block writes its partial tile and the last block to arrive
+// adds the shares in split order and runs the epilogue (a hand-off through
+// device-scope fences, tens of microseconds on this part).  The bf16 tile
+// kernel splits K without a hand-off: its blocks store raw partial tiles and
+// gemm_reduce_kernel, a second launch, adds them in split order and runs the
+// epilogue -- used for the long-K projections whose tiles cannot fill the
+// chip on their own.
 //
 // Paired epilogues: the q/k weight rows of every head and the gate/up rows of
 // the MLP are stored interleaved in blocks of 16 (see the runtime's weight
