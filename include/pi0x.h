@@ -108,7 +108,8 @@ pi0x_status pi0x_expert_create(const pi0x_config* cfg, const void* weights_host,
  *   prefix_kv        device, cfg dtype, [depth][2][batch][prefix_len][head_dim]:
  *                    per layer the keys (index 0, already rotary-embedded at
  *                    their prefix positions) and values (index 1) of the
- *                    single kv head.  Read only.
+ *                    single kv head.  Read only; 16-byte aligned
+ *                    (PI0X_ERR_INVALID_ARG otherwise).
  *   prefix_valid_len device int32 [batch]: keys [0, v) of sample b are real,
  *                    [v, prefix_len) are padding and are never read.  Values
  *                    outside [0, prefix_len] are clamped into it.  The suffix

@@ -240,6 +240,10 @@ def test_call_argument_errors(tiny):
     assert b.pi0x_denoise(*args(1, 17)) == b.PI0X_ERR_CAPACITY
     assert b.pi0x_denoise(*args(2, 2)) == b.PI0X_ERR_CAPACITY
     assert b.pi0x_denoise(*args(0, 2)) == b.PI0X_ERR_INVALID_ARG
+    bad = list(args(1, 2))
+    bad[3] += 4  # a misaligned prefix cache is rejected before anything is enqueued
+    assert b.pi0x_denoise(*bad) == b.PI0X_ERR_INVALID_ARG
+    assert "aligned" in b.pi0x_last_error()
 
 
 # ---------------------------------------------------------------------------

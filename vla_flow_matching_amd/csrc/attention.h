@@ -338,19 +338,21 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // Merges the split partial softmax states of attn_kernel in split order.
-// Grid (tiles, B, head_dim / 16), 512 threads: slot s = QT-tile t * NT +
-// thread of attn_kernel (the query and the lanes it held there), 4 output
-// features of d-tile blockIdx.z.
+// Grid (4 * tiles, B, head_dim / 16), 128 threads: slot s = QT-tile t * NT +
+// thread of attn_kernel (the query and the lanes it held there) is thread
+// s % 128 of block 4 * tile + s / 128, and takes 4 output features of d-tile
+// blockIdx.z.  Quarter-size blocks spread the partial reads over 4x as many
+// CUs as one block per query tile would.
 template <int DH> constexpr int attn_combine_chunks() { return DH / 16; }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   constexpr int NW = AttnCfg<T>::NW, QT = AttnCfg<T>::QT, NT = NW * 64;
   constexpr int ND = DH / 16, NR = 2 + ND * 4;
   static_assert(QT * NT == 512, "one combine thread per attention slot");
-  const int slot = threadIdx.x, t = slot / NT, tid = slot % NT;
+  const int slot = (int)(blockIdx.x % 4) * 128 + (int)threadIdx.x, t = slot / NT, tid = slot % NT;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z;
+  const int tile = blockIdx.x / 4, b = blockIdx.y, d0 = blockIdx.z;
   const int nq = a.nh * a.S;
   const int qi = tile * kAttnQueries + (wave * QT + t) * 16 + (lane & 15);
   if (qi >= nq) return;
@@ -404,26 +406,41 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs a) {
 
 // Prefix values, transposed once per call: vt[l][b][d][vt_pos(key)] =
 // V_l[b][key][d] for keys < valid_len[b], 0 for the rest (padded keys are not
-// read).  32 keys x 64
-// features per block through LDS.
+// read).  64 keys x 64 features per block through LDS, 16 bytes per global
+// access on both sides: key rows are read as vectors, and each output vector
+// holds 8 (bf16) or 4 (float32) consecutive vt_pos positions of one feature,
+// gathered from the LDS tile.  Lp is a multiple of 64, so a block's 64 keys
+// are two whole vt_pos groups.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const CallDesc* __restrict__ desc, int B, int L, int DH,
                                                           int Lp, T* __restrict__ vt) {
-  __shared__ T tileb[32][64 + 1];
-  const int k0 = blockIdx.x * 32, d0 = blockIdx.y * 64, lb = blockIdx.z;  // lb = layer * B + b
+  constexpr int VE = 16 / (int)sizeof(T), KB = 64, DB = 64, LD = DB + VE;
+  __shared__ __attribute__((aligned(16))) T tileb[KB * LD];
+  const int k0 = blockIdx.x * KB, d0 = blockIdx.y * DB, lb = blockIdx.z;  // lb = layer * B + b
   const int layer = lb / B, b = lb - layer * B;
   int valid = desc->valid[b];
   valid = valid < 0 ? 0 : (valid > L ? L : valid);
   const T* src = reinterpret_cast<const T*>(desc->kv) + (((size_t)layer * 2 + 1) * B + b) * (size_t)L * DH;
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-    const int kk = i / 64, dd = i % 64, key = k0 + kk;
-    tileb[kk][dd] = (key < valid && d0 + dd < DH) ? src[(size_t)key * DH + d0 + dd] : from_f32<T>(0.f);
+  for (int i = threadIdx.x; i < KB * DB / VE; i += 256) {
+    const int kk = i / (DB / VE), dv = (i % (DB / VE)) * VE, key = k0 + kk;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (key < valid && d0 + dv < DH) x = gload16(src + (size_t)key * DH + d0 + dv);
+    *reinterpret_cast<u32x4*>(&tileb[kk * LD + dv]) = x;
   }
   __syncthreads();
-  T* dst = vt + ((size_t)lb * DH) * Lp;
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-    const int dd = i / 32, kk = i % 32;
-    if (d0 + dd < DH) dst[(size_t)(d0 + dd) * Lp + vt_pos(k0 + kk)] = tileb[kk][dd];
+  T* dst = vt + ((size_t)lb * DH) * Lp + k0;
+  for (int i = threadIdx.x; i < DB * KB / VE; i += 256) {
+    const int dd = i / (KB / VE), p0 = (i % (KB / VE)) * VE;
+    if (d0 + dd >= DH) continue;
+    T v[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      // position p = 32 c + 8 g + 4 h + r holds key 32 c + 16 h + 4 g + r
+      const int p = p0 + e;
+      const int key = (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+      v[e] = tileb[key * LD + dd];
+    }
+    *reinterpret_cast<u32x4*>(dst + (size_t)(d0 + dd) * Lp + p0) = __builtin_bit_cast(u32x4, v);
   }
 }
 

@@ -469,7 +469,7 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   attn_kernel<T, DH><<<dim3(8 * ((units + 7) / 8)), dim3(AttnCfg<T>::NW * 64), smem, s>>>(a);
   PI0X_HIP(hipGetLastError());
   if (a.splits > 1) {
-    attn_combine_kernel<T, DH><<<dim3(tiles, B, attn_combine_chunks<DH>()), dim3(512), 0, s>>>(a);
+    attn_combine_kernel<T, DH><<<dim3(4 * tiles, B, attn_combine_chunks<DH>()), dim3(128), 0, s>>>(a);
     PI0X_HIP(hipGetLastError());
   }
   return PI0X_OK;
@@ -508,7 +508,7 @@ template <typename T>
 pi0x_status launch_transpose_v(pi0x_expert* h, hipStream_t s, int B, int L) {
   if (L <= 0) return PI0X_OK;
   const int Lp = prefix_pad(L);
-  hipLaunchKernelGGL((transpose_v_kernel<T>), dim3(Lp / 32, (h->dh + 63) / 64, h->D * B), dim3(256), 0, s, h->desc, B,
+  hipLaunchKernelGGL((transpose_v_kernel<T>), dim3(Lp / 64, (h->dh + 63) / 64, h->D * B), dim3(256), 0, s, h->desc, B,
                      L, h->dh, Lp, reinterpret_cast<T*>(h->vtp));
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
@@ -1103,6 +1103,8 @@ pi0x_status check_call(pi0x_expert* h, int32_t batch, int32_t prefix_len, const 
   if (!h) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
   if (!valid || !state || !xin || !out) return fail(PI0X_ERR_INVALID_ARG, "a device pointer argument is NULL");
   if (prefix_len > 0 && !prefix_kv) return fail(PI0X_ERR_INVALID_ARG, "prefix_kv is NULL");
+  if (prefix_len > 0 && reinterpret_cast<uintptr_t>(prefix_kv) % 16 != 0)
+    return fail(PI0X_ERR_INVALID_ARG, "prefix_kv must be 16-byte aligned");
   if (batch < 1) return fail(PI0X_ERR_INVALID_ARG, "batch must be >= 1");
   if (prefix_len < 0) return fail(PI0X_ERR_INVALID_ARG, "prefix_len must be >= 0");
   if (batch > h->Bmax) return fail(PI0X_ERR_CAPACITY, "batch exceeds max_batch");
