@@ -60,7 +60,8 @@ struct AttnArgs {
   int causal;  // suffix mask: 0 pi0 block rule, 1 lower triangle
   int prefill;  // prefix pass: prefix keys only
   int splits, tiles;
-  float* partial;  // splits > 1: [B][tiles][splits][QT][2 + head_dim/4][threads], 512 per (query tile, field)
+  float* partial;  // splits > 1, per (B, tile, split, QT-tile): float32 max and sum [2][threads],
+                   // then the unnormalised outputs in the model dtype [head_dim/16][threads][4]
 };
 
 // Per dtype: KB keys per staged block, NW waves per block, QT 16-query tiles
@@ -97,6 +98,24 @@ __device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r
 // exp for the softmax: the hardware exp2 path in bf16 mode, libm expf in float32 mode.
 template <typename T> __device__ __forceinline__ float fexp(float x) { return expf(x); }
 template <> __device__ __forceinline__ float fexp<bf16>(float x) { return __expf(x); }
+
+// Four consecutive split-partial outputs as one access: 16 bytes of float32
+// or 8 bytes of bf16 (the bf16 path keeps its unnormalised partial outputs in
+// bf16, halving the split traffic; the maxima and sums stay float32).
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+}
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+}
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  v[0] = to_f32(x[0]); v[1] = to_f32(x[1]); v[2] = to_f32(x[2]); v[3] = to_f32(x[3]);
+}
 
 template <typename T, int DH>
 __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
@@ -321,10 +340,10 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
       float* mine = a.partial + (((size_t)b * a.tiles + tile) * a.splits + split) * (QT * NR * NT) + (size_t)t * NR * NT;
       mine[tid] = m_run[t];
       mine[NT + tid] = l_tot;
+      // the unnormalised outputs in the model dtype: [d-tile][thread][4]
+      T* po = reinterpret_cast<T*>(mine + 2 * NT) + (size_t)tid * 4;
 #pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mine[(2 + d * 4 + e) * NT + tid] = o[t][d][e];
+      for (int d = 0; d < ND; ++d) store4(po + (size_t)d * NT * 4, o[t][d]);
       continue;
     }
     if (!qok[t]) continue;
@@ -373,8 +392,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
         const float* pz = P + (size_t)min(z0 + k, a.splits - 1) * QT * NR * NT;
         vm[k] = pz[0];
         vl[k] = pz[NT];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vo[k][e] = pz[(2 + d0 * 4 + e) * NT];
+        load4(reinterpret_cast<const T*>(pz - tid + 2 * NT) + ((size_t)d0 * NT + tid) * 4, vo[k]);
       }
       float mb = m;
 #pragma unroll
