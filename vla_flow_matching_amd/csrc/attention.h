@@ -72,7 +72,14 @@ struct AttnArgs {
 template <typename T> struct AttnCfg;
 template <> struct AttnCfg<bf16> { static constexpr int KB = 64, NW = 8, QT = 1; };
 template <> struct AttnCfg<float> { static constexpr int KB = 32, NW = 8, QT = 1; };
-constexpr int kAttnQueries = 128;  // queries per block
+constexpr int kAttnQueries = 128;  // queries per block (at most)
+
+// First 16-query tile of block `tile` when the ceil(nq / 16) tiles of a
+// sample are dealt out evenly over `tiles` blocks (tiles = ceil(nq / 128), so
+// no block gets more than 128 queries).
+__host__ __device__ __forceinline__ int attn_wave_tile0(int tile, int nq, int tiles) {
+  return (int)((long)tile * ((nq + 15) / 16) / tiles);
+}
 
 // LDS layout.  bf16 (head_dim a multiple of 64): unpadded 128-byte rows --
 // K split into head_dim/64 sub-tiles [KB][64], V^T [head_dim][KB = 64] -- with
@@ -141,12 +148,17 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
   if (u >= units) return;
   const int tile = u % a.tiles, split = (u / a.tiles) % a.splits, b = u / (a.tiles * a.splits);
   const int nq = a.nh * a.S;
+  // the sample's 16-query tiles are dealt out evenly over its blocks (at 408
+  // queries: 6, 7, 6, 7 of 8 waves), and a wave past its block's share skips
+  // the score and PV work, so no block carries more waves of work than needed
+  const int wt0 = attn_wave_tile0(tile, nq, a.tiles), wt1 = attn_wave_tile0(tile + 1, nq, a.tiles);
+  const bool wact = wt0 + wave * QT < wt1;
   int qs[QT], qn[QT];
   bool qok[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const int qi = tile * kAttnQueries + (wave * QT + t) * 16 + (lane & 15);
-    qok[t] = qi < nq;
+    const int wt = wt0 + wave * QT + t, qi = wt * 16 + (lane & 15);
+    qok[t] = wt < wt1 && qi < nq;
     qs[t] = qok[t] ? qi / a.nh : 0;
     qn[t] = qok[t] ? qi - qs[t] * a.nh : 0;
   }
@@ -248,6 +260,7 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
     const T* ks = Ks + st * KB * LDK;
     const T* vt = Vt + st * DH * LDV;
     const bool pre = blk < nb_pre;
+    if (wact) {
     const int base = pre ? blk * KB : (blk - nb_pre) * KB;
     const int lim = pre ? valid : a.S;
 
@@ -325,12 +338,14 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
         for (int t = 0; t < QT; ++t) mma32(vf, pf[t], o[t][d]);
       }
     }
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (more) sstore(st ^ 1);
     st ^= 1;
   }
 
   // lane holds O[q][d*16 + 4g + e] (unnormalised) of its query in each tile
+  if (!wact) return;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     float l_tot = l_run[t] + __shfl_xor(l_run[t], 16, 64);
@@ -373,8 +388,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4;
   const int tile = blockIdx.x / 4, b = blockIdx.y, d0 = blockIdx.z;
   const int nq = a.nh * a.S;
-  const int qi = tile * kAttnQueries + (wave * QT + t) * 16 + (lane & 15);
-  if (qi >= nq) return;
+  const int wt = attn_wave_tile0(tile, nq, a.tiles) + wave * QT + t, qi = wt * 16 + (lane & 15);
+  if (wt >= attn_wave_tile0(tile + 1, nq, a.tiles) || qi >= nq) return;
   const int qs = qi / a.nh, qn = qi - qs * a.nh;
   const float* P = a.partial + ((size_t)b * a.tiles + tile) * a.splits * (QT * NR * NT) + (size_t)t * NR * NT + tid;
   // splits in batches of ZC (4, 8 or 16, the smallest that covers the splits):
