@@ -231,6 +231,27 @@ def test_tiny_bf16_zero_and_one_valid_prefix():
         c.ex.close()
 
 
+def test_graph_cache_eviction_records_again(tiny):
+    """More distinct (prefix length, steps) keys than the handle keeps graphs
+    for: the oldest graphs are destroyed and recorded again when their key
+    comes back, with bitwise the same result."""
+    d = tiny.dev
+    keys = [(L, N) for L in (64, 40) for N in range(1, 17)] + [(24, 1), (24, 2), (24, 3)]
+    assert len(keys) > 32
+    first = {}
+    for L, N in keys:
+        kv = d["prefix_kv"][:, :, :, :L].contiguous()
+        valid = torch.clamp(d["valid_len"], max=L)
+        first[(L, N)] = tiny.ex.denoise(kv, valid, d["state"], d["noise"], N).cpu().numpy()
+    _say(f"{len(keys)} graph keys recorded; replaying the evicted ones")
+    for L, N in keys[:4]:
+        kv = d["prefix_kv"][:, :, :, :L].contiguous()
+        valid = torch.clamp(d["valid_len"], max=L)
+        again = tiny.ex.denoise(kv, valid, d["state"], d["noise"], N).cpu().numpy()
+        assert np.array_equal(again, first[(L, N)]), (L, N)
+    check_close(first[(TINY.prefix_len, 1)], tiny.ref(num_steps=1), "fp32", "tiny fp32 N=1 after eviction")
+
+
 def test_call_argument_errors(tiny):
     from vla_flow_matching_amd import binding as b
     d = tiny.dev

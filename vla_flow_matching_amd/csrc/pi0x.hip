@@ -643,6 +643,9 @@ pi0x_status run_graph(pi0x_expert* h, const Key& key, F launch_eager, hipStream_
   auto it = h->graphs.find(key);
   if (it == h->graphs.end()) {
     if ((int)h->graphs.size() >= kMaxGraphs) {
+      // the oldest graph may still be replaying from an earlier call: let the
+      // device drain before its executable is destroyed
+      PI0X_HIP(hipDeviceSynchronize());
       const Key old = h->graph_order.front();
       h->graph_order.erase(h->graph_order.begin());
       auto o = h->graphs.find(old);
