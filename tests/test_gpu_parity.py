@@ -302,6 +302,19 @@ def test_full_bf16_b2_partial_row_tile_and_key_splits():
         c.ex.close()
 
 
+def test_full_bf16_b1_longest_prefix():
+    # prefix_len 1024 (the default max_prefix_len): 16 prefix key blocks + 1
+    # suffix block, so attention splits the keys 17 ways and the combine
+    # merges them in two batches of loads, carrying the running maximum over
+    w = synth.WORKLOADS["pi0_bf16_b1"].replace(name="pi0_bf16_b1_l1024", prefix_len=1024, seed=4)
+    c = Case(w)
+    try:
+        out = c.run()
+        check_close(out, c.ref(), "bf16", "pi0 bf16 B=1 L=1024 N=10")
+    finally:
+        c.ex.close()
+
+
 def test_full_bf16_b64_sampled_parity():
     c = Case(synth.WORKLOADS["pi0_bf16_b64"])
     try:
