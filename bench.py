@@ -380,7 +380,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "prefix_len": w.prefix_len, "num_steps": w.num_steps,
-                   "horizon": w.shape.horizon, "action_dim": w.shape.action_dim, "expert": "gemma_300m shape"},
+                   "horizon": w.shape.horizon, "action_dim": w.shape.action_dim, "layers": w.shape.depth, "width": w.shape.width},
         "roofline": main_res["roofline"],
         "whole_loop": main_res["whole_loop"],
         "kernels": main_res["kernels"],
