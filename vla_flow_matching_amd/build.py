@@ -19,16 +19,31 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+DRIVER_SRC = os.path.join(PKG, "csrc", "denoise_driver.cpp")
+DRIVER = os.path.join(PKG, "denoise_driver")
+
+
+def _run(cmd: list[str]) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        raise RuntimeError(f"{os.path.basename(cmd[0])} failed ({res.returncode}):\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    out = _run([HIPCC, *FLAGS, SRC, "-o", tmp])
     if verbose and out.strip():
         print(out, file=sys.stderr)
     os.replace(tmp, LIB)
+    # the C++ driver of the ABI (host code only), linked against the library beside it
+    dtmp = DRIVER + ".tmp"
+    out = _run([HIPCC, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), DRIVER_SRC,
+                "-L", PKG, "-lpi0x", "-Wl,-rpath,$ORIGIN", "-o", dtmp])
+    if verbose and out.strip():
+        print(out, file=sys.stderr)
+    os.replace(dtmp, DRIVER)
     return LIB
 
 
