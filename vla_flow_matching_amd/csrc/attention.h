@@ -124,10 +124,10 @@ __device__ __forceinline__ void load4(const bf16* p, float* v) {
   v[0] = to_f32(x[0]); v[1] = to_f32(x[1]); v[2] = to_f32(x[2]); v[3] = to_f32(x[3]);
 }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
-  constexpr int KB = AttnCfg<T>::KB, NW = AttnCfg<T>::NW, QT = AttnCfg<T>::QT, NT = NW * 64;
-  static_assert(NW * QT * 16 == kAttnQueries, "queries per block");
+template <typename T, int DH, int NW = AttnCfg<T>::NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  constexpr int KB = AttnCfg<T>::KB, QT = AttnCfg<T>::QT, NT = NW * 64;
+  static_assert(NW * QT * 16 <= kAttnQueries, "queries per block");
   constexpr int KT = KB / 16;   // 16-key score tiles per block
   constexpr int KS = KB / 32;   // 32-key PV steps per block
   constexpr int VE = 16 / (int)sizeof(T);
@@ -372,21 +372,21 @@ __global__ __launch_bounds__(AttnCfg<T>::NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // Merges the split partial softmax states of attn_kernel in split order.
-// Grid (4 * tiles, B, head_dim / 16), 128 threads: slot s = QT-tile t * NT +
-// thread of attn_kernel (the query and the lanes it held there) is thread
-// s % 128 of block 4 * tile + s / 128, and takes 4 output features of d-tile
-// blockIdx.z.  Quarter-size blocks spread the partial reads over 4x as many
-// CUs as one block per query tile would.
+// Grid (CB * tiles, B, head_dim / 16) with CB = QT * NT / 128 blocks of 128
+// threads per query tile: slot s = QT-tile t * NT + thread of attn_kernel (the
+// query and the lanes it held there) is thread s % 128 of block CB * tile +
+// s / 128, and takes 4 output features of d-tile blockIdx.z.  Small blocks
+// spread the partial reads over more CUs than one block per query tile would.
 template <int DH> constexpr int attn_combine_chunks() { return DH / 16; }
 
-template <typename T, int DH>
+template <typename T, int DH, int NW = AttnCfg<T>::NW>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  constexpr int NW = AttnCfg<T>::NW, QT = AttnCfg<T>::QT, NT = NW * 64;
+  constexpr int QT = AttnCfg<T>::QT, NT = NW * 64, CB = QT * NT / 128;  // combine blocks per query tile
   constexpr int ND = DH / 16, NR = 2 + ND * 4;
-  static_assert(QT * NT == 512, "one combine thread per attention slot");
-  const int slot = (int)(blockIdx.x % 4) * 128 + (int)threadIdx.x, t = slot / NT, tid = slot % NT;
+  static_assert(QT * NT % 128 == 0, "whole combine blocks per attention block");
+  const int slot = (int)(blockIdx.x % CB) * 128 + (int)threadIdx.x, t = slot / NT, tid = slot % NT;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int tile = blockIdx.x / 4, b = blockIdx.y, d0 = blockIdx.z;
+  const int tile = blockIdx.x / CB, b = blockIdx.y, d0 = blockIdx.z;
   const int nq = a.nh * a.S;
   const int wt = attn_wave_tile0(tile, nq, a.tiles) + wave * QT + t, qi = wt * 16 + (lane & 15);
   if (wt >= attn_wave_tile0(tile + 1, nq, a.tiles) || qi >= nq) return;
