@@ -102,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.pi0x_set_timing.restype = i32
         L.pi0x_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.pi0x_read_timing.restype = i32
+        L.pi0x_stack_trace_layout.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.pi0x_stack_trace_layout.restype = i32
+        L.pi0x_set_stack_trace.argtypes = [vp, vp, sz]
+        L.pi0x_set_stack_trace.restype = i32
         L.pi0x_prefix_config_default.argtypes = [P]
         L.pi0x_prefix_config_default.restype = None
         L.pi0x_prefix_weight_count.argtypes = [P]
@@ -194,7 +198,8 @@ def pi0x_prefix_read_timing(p) -> tuple[int, dict]:
     return st, {k: (tot[i], int(cnt[i])) for i, k in enumerate(KERNEL_CLASSES)}
 
 
-KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final"]
+KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final",
+                  "layer_stack"]
 
 
 def norm_struct(stats: dict | None):
@@ -235,6 +240,16 @@ def pi0x_read_timing(h) -> tuple[int, dict]:
     return st, {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
 
 
+def pi0x_stack_trace_layout(h) -> tuple[int, int, int]:
+    blocks, layers = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().pi0x_stack_trace_layout(h, ctypes.byref(blocks), ctypes.byref(layers))
+    return st, blocks.value, layers.value
+
+
+def pi0x_set_stack_trace(h, trace_ptr, nbytes: int) -> int:
+    return lib().pi0x_set_stack_trace(h, trace_ptr, nbytes)
+
+
 def check(status: int) -> None:
     if status != PI0X_OK:
         raise Pi0xError(status, pi0x_last_error())
@@ -254,13 +269,43 @@ def make_config(shape, dtype: str = "bf16", max_batch: int = 64, max_prefix_len:
     return c
 
 
+def check_tensor(name: str, t, dtype, shape: tuple, device) -> None:
+    """Raises ValueError unless t is a contiguous torch tensor of dtype and shape
+    on device (the layout the C entry points assume for a raw pointer)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _overlaps(a, b) -> bool:
+    if a is None or b is None:
+        return False
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
+def model_dtype(cfg: pi0x_config):
+    import torch
+    return torch.bfloat16 if cfg.dtype == PI0X_BF16 else torch.float32
+
+
 class Expert:
-    """Owns a pi0x handle; calls take torch device tensors."""
+    """Owns a pi0x handle; calls take torch device tensors (validated here:
+    dtype, shape, contiguity and device, before any pointer reaches the C ABI)."""
 
     def __init__(self, cfg: pi0x_config, weights: np.ndarray):
-        import torch  # noqa: F401  (device memory and streams come from torch)
+        import torch  # (device memory and streams come from torch)
         w = np.ascontiguousarray(weights, dtype=np.float32)
         self.cfg = cfg
+        self.device = torch.device("cuda", torch.cuda.current_device())
         st, self.h = pi0x_expert_create(cfg, w.ctypes.data, w.nbytes)
         check(st)
 
@@ -272,12 +317,40 @@ class Expert:
     def _ptr(t):
         return t.data_ptr() if t is not None else None
 
-    def denoise(self, prefix_kv, valid_len, state, noise, num_steps: int, out=None, stream=None):
+    def _validate(self, prefix_kv, valid_len, state, x, out, extra=(), alias_ok=None):
+        """Shapes from state: B = state.shape[0]; the prefix length from
+        prefix_kv [depth][2][B][L][head_dim] (None: an empty prefix).  Returns (B, L)."""
         import torch
-        B = state.shape[0]
-        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
-        if out is None:
+        c, dev = self.cfg, self.device
+        if not isinstance(state, torch.Tensor) or state.dim() != 2:
+            raise ValueError("state must be a 2-D torch tensor [batch][state_dim]")
+        B = int(state.shape[0])
+        check_tensor("state", state, torch.float32, (B, c.state_dim), dev)
+        check_tensor("valid_len", valid_len, torch.int32, (B,), dev)
+        L = 0
+        if prefix_kv is not None:
+            if not isinstance(prefix_kv, torch.Tensor) or prefix_kv.dim() != 5:
+                raise ValueError("prefix_kv must be a 5-D torch tensor [depth][2][batch][prefix_len][head_dim]")
+            L = int(prefix_kv.shape[3])
+            check_tensor("prefix_kv", prefix_kv, model_dtype(c), (c.depth, 2, B, L, c.head_dim), dev)
+        chunk = (B, c.action_horizon, c.action_dim)
+        check_tensor("x", x, torch.float32, chunk, dev)
+        check_tensor("out", out, torch.float32, chunk, dev)
+        for name, t in extra:
+            check_tensor(name, t, torch.float32, chunk, dev)
+        for name, t in [("prefix_kv", prefix_kv), ("valid_len", valid_len), ("state", state), ("x", x)] + list(extra):
+            if t is alias_ok and t is not None and t.data_ptr() == out.data_ptr():
+                continue
+            if _overlaps(out, t):
+                raise ValueError(f"out must not overlap {name}")
+        return B, L
+
+    def denoise(self, prefix_kv, valid_len, state, noise, num_steps: int, out=None, stream=None):
+        """out may be noise itself (the loop copies x first); no other overlap."""
+        import torch
+        if out is None and isinstance(noise, torch.Tensor):
             out = torch.empty_like(noise)
+        B, L = self._validate(prefix_kv, valid_len, state, noise, out, alias_ok=noise)
         check(pi0x_denoise(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                            self._ptr(noise), int(num_steps), self._ptr(out), self._stream(stream)))
         return out
@@ -288,10 +361,14 @@ class Expert:
         """The loop variants of pi0x_denoise_ex; dof_mask / padding_action: float32
         device tensors [B][H][A] (both or neither)."""
         import torch
-        B = state.shape[0]
-        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
-        if out is None:
+        if out is None and isinstance(noise, torch.Tensor):
             out = torch.empty_like(noise)
+        if (dof_mask is None) != (padding_action is None):
+            raise ValueError("dof_mask and padding_action go together")
+        extra = [] if dof_mask is None else [("dof_mask", dof_mask), ("padding_action", padding_action)]
+        B, L = self._validate(prefix_kv, valid_len, state, noise, out, extra=extra, alias_ok=noise)
+        if schedule not in SCHEDULES:
+            raise ValueError(f"unknown schedule {schedule!r}")
         opts = pi0x_loop_options(SCHEDULES[schedule], int(bool(x_prediction)), int(bool(causal_actions)),
                                  self._ptr(dof_mask), self._ptr(padding_action))
         check(pi0x_denoise_ex(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
@@ -300,10 +377,9 @@ class Expert:
 
     def denoise_step(self, prefix_kv, valid_len, state, x_t, t: float, out=None, stream=None):
         import torch
-        B = state.shape[0]
-        L = prefix_kv.shape[3] if prefix_kv is not None and prefix_kv.dim() > 3 else 0
-        if out is None:
+        if out is None and isinstance(x_t, torch.Tensor):
             out = torch.empty_like(x_t)
+        B, L = self._validate(prefix_kv, valid_len, state, x_t, out)
         check(pi0x_denoise_step(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                                 self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
         return out
@@ -351,22 +427,34 @@ class PrefixModel:
     """Owns a pi0x prefix-pass handle; calls take torch device tensors."""
 
     def __init__(self, cfg: pi0x_config, weights: np.ndarray):
-        import torch  # noqa: F401
+        import torch
         w = np.ascontiguousarray(weights, dtype=np.float32)
         self.cfg = cfg
+        self.device = torch.device("cuda", torch.cuda.current_device())
         st, self.h = pi0x_prefix_create(cfg, w.ctypes.data, w.nbytes)
         check(st)
 
     def prefill(self, embeddings, valid_len, out=None, stream=None):
         """embeddings [B][L][width] (model dtype) -> cache [depth][2][B][L][head_dim]."""
         import torch
-        B, L = embeddings.shape[0], embeddings.shape[1]
-        c = self.cfg
+        c, dev, dt = self.cfg, self.device, model_dtype(self.cfg)
+        if not isinstance(embeddings, torch.Tensor) or embeddings.dim() != 3:
+            raise ValueError("embeddings must be a 3-D torch tensor [batch][prefix_len][width]")
+        B, L = int(embeddings.shape[0]), int(embeddings.shape[1])
+        check_tensor("embeddings", embeddings, dt, (B, L, c.width), dev)
+        check_tensor("valid_len", valid_len, torch.int32, (B,), dev)
         if out is None:
-            out = torch.empty((c.depth, 2, B, L, c.head_dim), dtype=embeddings.dtype, device=embeddings.device)
-        s = (stream or torch.cuda.current_stream()).cuda_stream
-        check(pi0x_prefill(self.h, B, L, embeddings.data_ptr(), valid_len.data_ptr(), out.data_ptr(), s))
+            out = torch.empty((c.depth, 2, B, L, c.head_dim), dtype=dt, device=dev)
+        check_tensor("out", out, dt, (c.depth, 2, B, L, c.head_dim), dev)
+        if _overlaps(out, embeddings) or _overlaps(out, valid_len):
+            raise ValueError("out must not overlap the inputs")
+        check(pi0x_prefill(self.h, B, L, embeddings.data_ptr(), valid_len.data_ptr(), out.data_ptr(),
+                           self._stream(stream)))
         return out
+
+    def _stream(self, stream):
+        import torch
+        return (stream or torch.cuda.current_stream()).cuda_stream
 
     def set_timing(self, enable: bool):
         check(pi0x_prefix_set_timing(self.h, enable))

@@ -536,10 +536,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, Epi epi) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mine[((i * TN + j) * 4 + e) * 256 + tid] = acc[i][j][e];
-    // hand-off: the block's stores complete at the barrier, one thread publishes
+    // hand-off: every thread makes its own partial stores visible at device
+    // scope before the barrier, then one thread publishes the arrival
+    __threadfence();
     __syncthreads();
     if (tid == 0) {
-      __threadfence();
       s_last = atomicAdd(&g.counters[tile], 1u) == (unsigned)g.splits - 1u;
       __threadfence();
     }
