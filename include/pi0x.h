@@ -234,33 +234,11 @@ typedef enum {
   PI0X_KERNEL_GATE_UP = 5,      /* gate/up projection + GeGLU */
   PI0X_KERNEL_DOWN = 6,         /* down projection + residual */
   PI0X_KERNEL_FINAL = 7,        /* final norm + action_out_proj + Euler update */
-  PI0X_KERNEL_LAYER_STACK = 8,  /* batch 1, bf16: every expert layer of one Euler step in one
-                                   persistent kernel (replaces classes 2-6 there) */
-  PI0X_KERNEL_CLASSES = 9
+  PI0X_KERNEL_CLASSES = 8
 } pi0x_kernel_class;
 
 pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable);
 pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches);
-
-/*
- * Phase trace of the batch-1 persistent layer stack (class
- * PI0X_KERNEL_LAYER_STACK), for profiling.  pi0x_stack_trace_layout gives
- * the stack's grid (0 when the handle has no such stack) and depth.  While
- * timing is on and a trace buffer is set, every batch-1 call records, for its
- * first Euler step, device wall-clock stamps (100 MHz) into
- *   trace[((block * depth + layer) * 9 + phase) * 4 + k]
- * (device memory the caller owns, >= blocks * depth * 9 * 4 * 8 bytes):
- * phases 0-7 are the block's q/k/v, attention, merge, o_proj, o_proj
- * reduction, gate/up, down and down reduction units, k = 0 unit start, 1
- * dependency met, 2 weights landed, 3 completion published (stamps of units a
- * block does not run stay as they were); phase 8 is the block's weight
- * loader, k = 0 layer start, 1 after the q/k/v weights, 2 after the gate/up
- * weights, 3 after the layer's weights were issued.  trace == NULL turns it
- * off.  Errors: PI0X_ERR_SHAPE without a batch-1 stack, PI0X_ERR_CAPACITY for
- * a short buffer.
- */
-pi0x_status pi0x_stack_trace_layout(pi0x_expert* h, int32_t* blocks, int32_t* layers);
-pi0x_status pi0x_set_stack_trace(pi0x_expert* h, unsigned long long* trace, size_t bytes);
 
 /*
  * The prefix pass (page 1: sample_actions builds the prefix masks and

@@ -1,6 +1,6 @@
-"""The batch-1 persistent layer stack (bf16, the pi0 expert shape: every layer
-of an Euler step in one kernel, b1_stack.h) against the fp64 oracle, on the
-edge cases of its key blocks and on its determinism.
+"""The batch-1 path (bf16, the pi0 expert shape: the one-kernel wide GEMMs, the
+stream + reduce residual producers and the key-split attention) against the
+fp64 oracle, on the edge cases of its 64-key blocks and on its determinism.
 
 Bar: the loop's bf16 bar, max|diff| <= 3e-2 and relative L2 <= 1e-2."""
 from __future__ import annotations

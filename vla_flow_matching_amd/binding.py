@@ -102,10 +102,6 @@ def lib() -> ctypes.CDLL:
         L.pi0x_set_timing.restype = i32
         L.pi0x_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.pi0x_read_timing.restype = i32
-        L.pi0x_stack_trace_layout.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
-        L.pi0x_stack_trace_layout.restype = i32
-        L.pi0x_set_stack_trace.argtypes = [vp, vp, sz]
-        L.pi0x_set_stack_trace.restype = i32
         L.pi0x_prefix_config_default.argtypes = [P]
         L.pi0x_prefix_config_default.restype = None
         L.pi0x_prefix_weight_count.argtypes = [P]
@@ -198,8 +194,7 @@ def pi0x_prefix_read_timing(p) -> tuple[int, dict]:
     return st, {k: (tot[i], int(cnt[i])) for i, k in enumerate(KERNEL_CLASSES)}
 
 
-KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final",
-                  "layer_stack"]
+KERNEL_CLASSES = ["suffix_embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "final"]
 
 
 def norm_struct(stats: dict | None):
@@ -238,16 +233,6 @@ def pi0x_read_timing(h) -> tuple[int, dict]:
     cnt = (ctypes.c_int64 * n)()
     st = lib().pi0x_read_timing(h, ms, cnt)
     return st, {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
-
-
-def pi0x_stack_trace_layout(h) -> tuple[int, int, int]:
-    blocks, layers = ctypes.c_int32(), ctypes.c_int32()
-    st = lib().pi0x_stack_trace_layout(h, ctypes.byref(blocks), ctypes.byref(layers))
-    return st, blocks.value, layers.value
-
-
-def pi0x_set_stack_trace(h, trace_ptr, nbytes: int) -> int:
-    return lib().pi0x_set_stack_trace(h, trace_ptr, nbytes)
 
 
 def check(status: int) -> None:

@@ -45,7 +45,6 @@
 #include <vector>
 
 #include "attention.h"
-#include "b1_stack.h"
 #include "common.h"
 #include "gemm.h"
 #include "small_kernels.h"
@@ -149,15 +148,6 @@ struct pi0x_expert {
   unsigned* gemm_counters = nullptr;
   CallDesc* desc = nullptr;
   NormDev* norm = nullptr;  // boundary normalization statistics (all modes 0 at create)
-  // batch-1 layer stack as one persistent kernel per Euler step (b1_stack.h)
-  bool b1 = false;
-  const bf16** b1_lw = nullptr;  // [D][4] layer weights in fragment order (their own copies)
-  bf16* b1_kvf = nullptr;        // the call's prefix K/V in fragment order
-  float* b1_part = nullptr;      // o_proj and down K-slice partials
-  unsigned* b1_cnt = nullptr;    // dependency counters of a call
-  int b1_grid = 0;
-  unsigned long long* b1_trace = nullptr;  // caller's trace buffer (pi0x_set_stack_trace), used while timing
-  size_t b1_trace_bytes = 0;
   hipStream_t cap_stream = nullptr;
   std::map<Key, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
   std::vector<Key> graph_order;
@@ -561,46 +551,6 @@ float step_dt(int k, int N, bool zero_to_one) {
   return (float)((double)(k + 1) / (double)N) - (float)((double)k / (double)N);
 }
 
-__global__ void fill_u32_kernel(unsigned* p, size_t n, unsigned v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
-}
-
-// The batch-1 layer stack of Euler step k (b1_stack.h): every layer of the
-// expert in one launch; the counters were zeroed at the start of the call.
-pi0x_status launch_b1_stack(pi0x_expert* h, hipStream_t s, int L, int k, int causal) {
-  B1Args a;
-  a.lw = h->b1_lw;
-  a.D = h->D; a.W = h->W; a.M = h->M; a.nh = h->nh; a.S = h->S; a.qd = h->qd; a.nqkv = h->nqkv;
-  a.desc = h->desc;
-  a.L = L;
-  a.Lp = prefix_pad(L);
-  a.kvf = h->b1_kvf;
-  a.qk = reinterpret_cast<bf16*>(h->qk);
-  a.vts = reinterpret_cast<bf16*>(h->vts);
-  a.rope_cs = h->rope_cs;
-  a.hbuf = h->hbuf;
-  a.hb = reinterpret_cast<bf16*>(h->hb);
-  a.ssq = h->ssq;
-  a.np0 = h->W / kStreamGroup;
-  a.o = reinterpret_cast<bf16*>(h->o);
-  a.g = reinterpret_cast<bf16*>(h->gbuf);
-  a.apart = h->attn_partial;
-  a.cpart = h->b1_part;
-  a.dpart = h->b1_part + (size_t)(h->qd / 256) * h->S * h->W;
-  a.cnt = h->b1_cnt;
-  a.step = k;
-  a.nsplit = (L + 63) / 64 + 1;
-  a.ntile = (h->nh * h->S + 63) / 64;
-  a.causal = causal;
-  a.scale = 1.0f / 16.0f;
-  a.rms_eps = h->cfg.rms_eps;
-  a.trace = h->timing ? h->b1_trace : nullptr;
-  if (a.trace) b1_stack_kernel<true><<<dim3(h->b1_grid), dim3(kB1Threads), 0, s>>>(a);
-  else b1_stack_kernel<false><<<dim3(h->b1_grid), dim3(kB1Threads), 0, s>>>(a);
-  PI0X_HIP(hipGetLastError());
-  return PI0X_OK;
-}
-
 template <typename T>
 pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const LoopOpts& lo) {
   const int W = h->W, S = h->S, H = h->H, R = B * S, AR = B * H;
@@ -615,9 +565,6 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
   const int G = producer_group(bf, R);  // state-token copy, action-row MLP output, o_proj
   const int np = W / G;
   const NormIn nin{h->ssq, np};
-  // batch 1 in bf16: the layers of a step run as one persistent kernel, whose
-  // residual reductions write sum-of-squares partials per 32 columns
-  const bool b1 = bf && B == 1 && h->b1;
   // down (the longest-K residual producer): when its 128x64 tiles cannot fill
   // the chip (816 suffix rows at batch 16: 7 x 16 tiles) it runs as 128x128
   // tiles split over K (up to 8 ways, at most 512 blocks), reduced by
@@ -630,7 +577,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
     dsplit = std::min(8, 512 / (((R + 127) / 128) * (W / 128)));
     while (dsplit > 1 && (h->M / 64) % dsplit != 0) --dsplit;
   }
-  const int np_down = b1 ? W / 32 : (dsplit > 1 ? W / kStreamGroup : np);
+  const int np_down = dsplit > 1 ? W / kStreamGroup : np;
   const NormIn nin_down{h->ssq, np_down};
   auto down_proj = [&](const Layer& ly) -> pi0x_status {
     const EpiResidual<T> epi{h->hbuf, hb, W, h->ssq, np_down};
@@ -651,19 +598,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
   // time half of action_time_mlp_in (+ its bias) for every evaluated time
   PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
              (launch_gemm<T>(h, s, h->tau, W, h->w_tt, steps, W, W, EpiStore<float>{h->tbias, W, h->b_mi, 0})));
-  if (b1) {
-    // the persistent stack reads the prefix K/V in its own block order
-    auto pack_kv = [&]() -> pi0x_status {
-      if (L <= 0) return PI0X_OK;
-      hipLaunchKernelGGL(b1_pack_kv_kernel, dim3((L + 63) / 64, h->D), dim3(256), 0, s, h->desc, L, (L + 63) / 64,
-                         h->b1_kvf);
-      PI0X_HIP(hipGetLastError());
-      return PI0X_OK;
-    };
-    PI0X_TIMED(PI0X_KERNEL_ATTENTION, pack_kv());
-  } else {
-    PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_transpose_v<T>(h, s, B, L));
-  }
+  PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_transpose_v<T>(h, s, B, L));
   auto state_tok = [&]() -> pi0x_status {
     hipLaunchKernelGGL(state_token_kernel, dim3(B), dim3(256), 0, s, h->desc, h->norm, h->Sd, W, h->w_s, h->b_s,
                        h->hs);
@@ -678,10 +613,6 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
     return PI0X_OK;
   };
   PI0X_TIMED(PI0X_KERNEL_QKV_ROPE, rope_rows());
-  if (b1) {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(64), dim3(256), 0, s, h->b1_cnt, kB1CounterWords, 0u);
-    PI0X_HIP(hipGetLastError());
-  }
   const int nA = (AR + 3) / 4 * ((W + 255) / 256);
   for (int k = 0; k < steps; ++k) {
     const int first = (k == 0);
@@ -695,8 +626,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
     PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
                (launch_gemm<T>(h, s, h->u, W, h->w_mo, AR, W, W,
                                EpiSuffixRows<T>{h->hbuf, hb, W, H, S, h->b_mo, h->ssq, np}, NormIn(), R)));
-    if (b1) PI0X_TIMED(PI0X_KERNEL_LAYER_STACK, launch_b1_stack(h, s, L, k, lo.causal));
-    for (int l = 0; l < (b1 ? 0 : h->D); ++l) {
+    for (int l = 0; l < h->D; ++l) {
       const Layer& ly = h->layers[l];
       PI0X_TIMED(PI0X_KERNEL_QKV_ROPE,
                  (launch_gemm<T>(h, s, hA, W, ly.wqkv, R, h->nqkv, W,
@@ -1038,56 +968,6 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob, bool head) {
   return PI0X_OK;
 }
 
-// The persistent layer stack is off until it beats the kernel-per-phase
-// batch-1 path (measured: 2.0 vs 0.8 ms per Euler step).
-constexpr bool kB1StackOn = false;
-
-// The batch-1 persistent layer stack needs the pi0 expert's head layout
-// (head_dim 256, one kv head), every phase's unit count within its counters,
-// and one block of the kernel on every CU at once.
-pi0x_status setup_b1(pi0x_expert* h) {
-  h->b1 = false;
-  if (!kB1StackOn) return PI0X_OK;
-  if (!h->bf16() || h->dh != 256 || h->qd % 256 != 0 || h->W % 256 != 0 || h->W > 1024 ||
-      h->M % 512 != 0 || h->M / 512 > kB1MaxParts || h->qd / 256 > kB1MaxParts || h->S > 64 ||
-      (h->nh * h->S + 63) / 64 > kB1MaxTiles || (h->Lmax + 63) / 64 + 1 > kB1MaxSplits)
-    return PI0X_OK;
-  hipDeviceProp_t prop;
-  PI0X_HIP(hipGetDeviceProperties(&prop, h->device));
-  int per_cu = 0;
-  PI0X_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, b1_stack_kernel<false>, kB1Threads, 0));
-  if (per_cu < 1 || prop.multiProcessorCount < 8) return PI0X_OK;
-  h->b1_grid = prop.multiProcessorCount;  // one block per CU (the LDS ring takes most of a CU's LDS)
-  // fragment-order copies of every layer's weights
-  std::vector<const void*> lw((size_t)h->D * 4);
-  for (int l = 0; l < h->D; ++l) {
-    const void* src[4] = {h->layers[l].wqkv, h->layers[l].wo, h->layers[l].wgu, h->layers[l].wdown};
-    const int NK[4][2] = {{h->nqkv, h->W}, {h->W, h->qd}, {2 * h->M, h->W}, {h->W, h->M}};
-    for (int m = 0; m < 4; ++m) {
-      void* dst = nullptr;
-      PI0X_TRY(h->alloc(&dst, (size_t)NK[m][0] * NK[m][1] * 2));
-      hipLaunchKernelGGL(b1_pack_weights_kernel, dim3(1024), dim3(256), 0, 0, reinterpret_cast<const bf16*>(src[m]),
-                         NK[m][0], NK[m][1], reinterpret_cast<bf16*>(dst));
-      PI0X_HIP(hipGetLastError());
-      lw[4 * l + m] = dst;
-    }
-  }
-  {
-    void* kv = nullptr;
-    PI0X_TRY(h->alloc(&kv, (size_t)h->D * ((h->Lmax + 63) / 64) * 64 * 1024));
-    h->b1_kvf = reinterpret_cast<bf16*>(kv);
-  }
-  void* p = nullptr;
-  PI0X_TRY(h->alloc(&p, lw.size() * sizeof(void*)));
-  PI0X_HIP(hipMemcpy(p, lw.data(), lw.size() * sizeof(void*), hipMemcpyHostToDevice));
-  h->b1_lw = reinterpret_cast<const bf16**>(p);
-  PI0X_TRY(h->allocT(&h->b1_part, ((size_t)h->qd / 256 + h->M / 512) * h->S * h->W * 4));
-  PI0X_TRY(h->allocT(&h->b1_cnt, kB1CounterWords * 4));
-  PI0X_HIP(hipMemset(h->b1_cnt, 0, kB1CounterWords * 4));
-  h->b1 = true;
-  return PI0X_OK;
-}
-
 pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_expert* h) {
   h->cfg = *cfg;
   PI0X_HIP(hipGetDevice(&h->device));
@@ -1128,7 +1008,6 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
     PI0X_TRY(h->allocT(&h->gemm_counters, (size_t)kCounters * 4));
     PI0X_HIP(hipMemset(h->gemm_counters, 0, (size_t)kCounters * 4));
   }
-  PI0X_TRY(setup_b1(h));
   PI0X_TRY(h->allocT(&h->desc, sizeof(CallDesc)));
   PI0X_TRY(h->allocT(&h->norm, sizeof(NormDev)));
   {
@@ -1491,28 +1370,6 @@ pi0x_status pi0x_prefix_set_timing(pi0x_prefix_model* p, int32_t enable) {
 pi0x_status pi0x_prefix_read_timing(pi0x_prefix_model* p, double* total_ms, int64_t* launches) {
   if (!p) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
   return pi0x_read_timing(&p->core, total_ms, launches);
-}
-
-pi0x_status pi0x_stack_trace_layout(pi0x_expert* h, int32_t* blocks, int32_t* layers) {
-  if (!h || !blocks || !layers) return fail(PI0X_ERR_INVALID_ARG, "a pointer argument is NULL");
-  *blocks = h->b1 ? h->b1_grid : 0;
-  *layers = h->D;
-  return PI0X_OK;
-}
-
-pi0x_status pi0x_set_stack_trace(pi0x_expert* h, unsigned long long* trace, size_t bytes) {
-  if (!h) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
-  if (trace == nullptr) {
-    h->b1_trace = nullptr;
-    h->b1_trace_bytes = 0;
-    return PI0X_OK;
-  }
-  if (!h->b1) return fail(PI0X_ERR_SHAPE, "the handle has no batch-1 layer stack");
-  const size_t need = (size_t)h->b1_grid * h->D * 9 * 4 * sizeof(unsigned long long);
-  if (bytes < need) return fail(PI0X_ERR_CAPACITY, "trace buffer needs " + std::to_string(need) + " bytes");
-  h->b1_trace = trace;
-  h->b1_trace_bytes = bytes;
-  return PI0X_OK;
 }
 
 pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable) {
