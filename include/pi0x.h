@@ -128,6 +128,30 @@ pi0x_status pi0x_denoise(pi0x_expert* h, int32_t batch, int32_t prefix_len, cons
                          int32_t num_steps, float* actions_out, hipStream_t stream);
 
 /*
+ * pi0x_denoise for callers that cannot allocate device memory during a call:
+ * code under stream capture, tight serving loops and harnesses that forbid
+ * hipMalloc.  Same arguments, result and errors as pi0x_denoise, computed by
+ * the same kernels, but enqueued directly on `stream`: no graph is captured or
+ * instantiated and timing is ignored.  The call's working buffers (residual
+ * stream, activations, V^T copies, split partials, time features, call
+ * descriptor) come from one static device array of
+ * PI0X_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its load
+ * on that GPU until the process ends; the handle's own workspaces are not
+ * touched.  The call allocates nothing, on the device or in a library.
+ * Limits, checked before anything is enqueued: a bf16 handle
+ * (PI0X_ERR_DTYPE otherwise); at most 64 suffix rows, batch * (horizon + 1),
+ * i.e. batch 1 at the pi0 shape; the call's buffers within the array (the
+ * pi0 expert fits up to prefix_len 1024); PI0X_ERR_CAPACITY otherwise.
+ * Every call on one GPU shares the array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other
+ * handles, other threads) race and must be serialised by the caller.
+ */
+#define PI0X_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pi0x_status pi0x_denoise_noalloc(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                                 const int32_t* prefix_valid_len, const float* state, const float* noise,
+                                 int32_t num_steps, float* actions_out, hipStream_t stream);
+
+/*
  * One velocity evaluation (page 1, denoise_step): v = v_theta(x_t, t) for
  * every sample, with the same prefix/state arguments as pi0x_denoise.
  *   x_t    device float32 [batch][horizon][action_dim]

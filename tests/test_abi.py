@@ -15,7 +15,7 @@ from vla_flow_matching_amd import synth
 def test_library_exports_every_declared_function():
     names = b.declared_functions()
     assert set(names) == {"pi0x_config_default", "pi0x_weight_count", "pi0x_expert_create", "pi0x_denoise",
-                          "pi0x_denoise_step", "pi0x_expert_destroy", "pi0x_last_error", "pi0x_set_timing",
+                          "pi0x_denoise_noalloc", "pi0x_denoise_step", "pi0x_expert_destroy", "pi0x_last_error", "pi0x_set_timing",
                           "pi0x_read_timing", "pi0x_set_normalization", "pi0x_denoise_ex",
                           "pi0x_prefix_config_default", "pi0x_prefix_weight_count", "pi0x_prefix_create",
                           "pi0x_prefill", "pi0x_prefix_destroy", "pi0x_prefix_set_timing",
@@ -86,6 +86,7 @@ def test_create_rejects_null_pointers():
 def test_calls_reject_null_handle():
     assert b.pi0x_denoise(None, 1, 8, 1, 1, 1, 1, 2, 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_denoise_step(None, 1, 8, 1, 1, 1, 1, 0.5, 1, None) == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_denoise_noalloc(None, 1, 8, 1, 1, 1, 1, 2, 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_denoise_ex(None, 1, 8, 1, 1, 1, 1, 2, None, 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_denoise_ex(None, 1, 8, 1, 1, 1, 1, 2, b.pi0x_loop_options(), 1, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_set_timing(None, 1) == b.PI0X_ERR_INVALID_ARG

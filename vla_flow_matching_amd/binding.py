@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.pi0x_expert_create.restype = i32
         L.pi0x_denoise.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp]
         L.pi0x_denoise.restype = i32
+        L.pi0x_denoise_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.pi0x_denoise_noalloc.restype = i32
         L.pi0x_denoise_ex.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(pi0x_loop_options), vp, vp]
         L.pi0x_denoise_ex.restype = i32
         L.pi0x_denoise_step.argtypes = [vp, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp]
@@ -143,6 +145,10 @@ def pi0x_expert_create(cfg: pi0x_config, weights_ptr: int, weights_bytes: int) -
 
 def pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream) -> int:
     return lib().pi0x_denoise(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream)
+
+
+def pi0x_denoise_noalloc(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream) -> int:
+    return lib().pi0x_denoise_noalloc(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, out, stream)
 
 
 def pi0x_denoise_ex(h, batch, prefix_len, prefix_kv, valid, state, noise, num_steps, options, out, stream) -> int:
@@ -338,6 +344,14 @@ class Expert:
         B, L = self._validate(prefix_kv, valid_len, state, noise, out, alias_ok=noise)
         check(pi0x_denoise(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                            self._ptr(noise), int(num_steps), self._ptr(out), self._stream(stream)))
+        return out
+
+    def denoise_noalloc(self, prefix_kv, valid_len, state, noise, out, num_steps: int, stream=None):
+        """pi0x_denoise_noalloc: the caller passes the output buffer too; the
+        call itself allocates nothing."""
+        B, L = self._validate(prefix_kv, valid_len, state, noise, out, alias_ok=noise)
+        check(pi0x_denoise_noalloc(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
+                                   self._ptr(noise), int(num_steps), self._ptr(out), self._stream(stream)))
         return out
 
     def denoise_ex(self, prefix_kv, valid_len, state, noise, num_steps: int, schedule: str = "pi0",

@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <type_traits>
@@ -144,6 +145,7 @@ struct pi0x_expert {
   float* stream_partial = nullptr;  // K-split partial tiles of the M <= 64 bf16 GEMMs
   size_t stream_partial_n = 0;
   float* attn_partial = nullptr;  // split attention states [blocks][2 + head_dim/4][512]
+  size_t attn_partial_n = 0;      // its float32 words
   float* split_partial = nullptr;  // K-split partial tiles of the bf16 tile GEMM (prefix pass)
   unsigned* gemm_counters = nullptr;
   CallDesc* desc = nullptr;
@@ -436,6 +438,19 @@ inline int attn_splits(int B, int tiles, int nblk) {
   return std::max(sp, 1);
 }
 
+// float32 words of the split partial states one attention launch writes: per
+// 128-query tile of a sample and key split, (2 + head_dim/4) x 512 (the
+// half-size 4-wave blocks hold half as many per tile and have twice the
+// tiles); 0 when the launch does not split.
+size_t attn_partial_floats(const pi0x_expert* h, int B, int L, int prefill) {
+  const int KB = h->bf16() ? AttnCfg<bf16>::KB : AttnCfg<float>::KB;
+  const int S = prefill ? L : h->S;
+  const int tiles = (h->nh * S + kAttnQueries - 1) / kAttnQueries;
+  const int nblk = (L + KB - 1) / KB + (prefill ? 0 : (h->S + KB - 1) / KB);
+  const int splits = attn_splits(B, tiles, nblk);
+  return splits > 1 ? (size_t)B * tiles * splits * (2 + h->dh / 4) * 512 : 0;
+}
+
 // prefill: the prefix pass, whose L prefix tokens are the queries and whose
 // keys are the layer's own (cache + the single-layer V^T buffer vtp).
 template <typename T, int DH>
@@ -466,6 +481,8 @@ pi0x_status launch_attn_dh(pi0x_expert* h, hipStream_t s, int B, int L, int laye
   const int nblk = (L + KB - 1) / KB + (prefill ? 0 : (h->S + KB - 1) / KB);
   constexpr size_t smem = attn_smem_bytes<T, DH>();
   a.partial = h->attn_partial;
+  if (attn_partial_floats(h, B, L, prefill) > h->attn_partial_n)
+    return fail(PI0X_ERR_SHAPE, "attention split partials exceed the workspace");
   // Key-split launches use half-size blocks (64 queries over 4 waves, one
   // wave per SIMD, twice the blocks) when that keeps the same number of key
   // splits: at batch 1, 98 blocks instead of 56 (attention + combine 14.6 ->
@@ -705,6 +722,124 @@ pi0x_status run(pi0x_expert* h, int B, int L, int N, const LoopOpts& lo, hipStre
     return h->bf16() ? enqueue<bf16>(h, s, B, L, N, lo) : enqueue<float>(h, s, B, L, N, lo);
   };
   return run_graph(h, Key{B, L, N, N > 0 ? 0 : 1, lo.bits()}, launch_eager, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The call variant that allocates nothing (pi0x_denoise_noalloc).  The call's
+// working buffers -- the residual stream, activations, V^T copies, split
+// partials, time features and the call descriptor -- are carved out of one
+// static device array instead of the handle's workspaces; the kernels are
+// the same and take the carved pointers as arguments.  The array's device
+// address is resolved once per GPU (scratch_lookup, from pi0x_expert_create,
+// with that GPU current): in host code the array's name is only a host-side
+// stand-in and is never passed to a kernel or a copy.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = PI0X_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+struct ScratchSlot {
+  bool looked_up = false;
+  void* ptr = nullptr;  // device address of scratch on this GPU
+  std::string err;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kScratchDevices];
+
+// once per device, with that device current
+void scratch_lookup(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (sl.looked_up) return;
+  sl.looked_up = true;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    sl.err = std::string("hipGetSymbolAddress of the scratch array: ") + hipGetErrorString(e);
+    return;
+  }
+  sl.ptr = p;
+}
+
+pi0x_status scratch_of(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || dev >= kScratchDevices || !g_scratch[dev].looked_up)
+    return fail(PI0X_ERR_INVALID_ARG, "no scratch array for this device (create the handle on it first)");
+  if (!g_scratch[dev].ptr) return fail(PI0X_ERR_HIP, g_scratch[dev].err);
+  *out = g_scratch[dev].ptr;
+  return PI0X_OK;
+}
+
+// the per-call buffers of a handle
+struct CallBufs {
+  float *hbuf, *ssq, *hs, *x, *tbias, *stream_partial, *attn_partial, *split_partial, *gemm_partial;
+  void *hb, *qk, *vts, *vtp, *o, *gbuf, *u, *tau;
+  unsigned* gemm_counters;
+  CallDesc* desc;
+  float2* rope_cs;
+  size_t stream_partial_n, attn_partial_n;
+};
+
+CallBufs bufs_of(const pi0x_expert* h) {
+  return CallBufs{h->hbuf, h->ssq, h->hs, h->x, h->tbias, h->stream_partial, h->attn_partial, h->split_partial,
+                  h->gemm_partial, h->hb, h->qk, h->vts, h->vtp, h->o, h->gbuf, h->u, h->tau, h->gemm_counters,
+                  h->desc, h->rope_cs, h->stream_partial_n, h->attn_partial_n};
+}
+
+void set_bufs(pi0x_expert* h, const CallBufs& b) {
+  h->hbuf = b.hbuf; h->ssq = b.ssq; h->hs = b.hs; h->x = b.x; h->tbias = b.tbias;
+  h->stream_partial = b.stream_partial; h->attn_partial = b.attn_partial; h->split_partial = b.split_partial;
+  h->gemm_partial = b.gemm_partial; h->hb = b.hb; h->qk = b.qk; h->vts = b.vts; h->vtp = b.vtp; h->o = b.o;
+  h->gbuf = b.gbuf; h->u = b.u; h->tau = b.tau; h->gemm_counters = b.gemm_counters; h->desc = b.desc;
+  h->rope_cs = b.rope_cs; h->stream_partial_n = b.stream_partial_n; h->attn_partial_n = b.attn_partial_n;
+}
+
+// Lays out the buffers of a bf16 call of B samples (B * S <= 64 rows: the
+// batch-1 kernels, which use no K-split tile partials), prefix length L and
+// `steps` evaluated times from base (nullptr: sizes only), each region
+// 256-byte aligned; returns the bytes the call needs.
+size_t carve_call_bufs(const pi0x_expert* h, int B, int L, int steps, char* base, CallBufs* b) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += std::max<size_t>((bytes + 255) / 256 * 256, 256);
+    return p;
+  };
+  const size_t R = (size_t)B * h->S, AR = (size_t)B * h->H, e = h->esz, W = h->W;
+  *b = CallBufs{};
+  b->hbuf = reinterpret_cast<float*>(take(R * W * 4));
+  b->hb = take(R * W * e);
+  b->ssq = reinterpret_cast<float*>(take(R * (W / 16) * 4));
+  b->qk = take(R * (h->qd + h->dh) * e);
+  b->vts = take((size_t)B * h->dh * h->Sp * e);
+  b->vtp = take((size_t)h->D * B * h->dh * prefix_pad(L) * e);
+  b->o = take(R * h->qd * e);
+  b->gbuf = take(R * h->M * e);
+  b->u = take(AR * W * e);
+  b->hs = reinterpret_cast<float*>(take((size_t)B * W * 4));
+  b->x = reinterpret_cast<float*>(take(AR * h->A * 4));
+  b->tau = take((size_t)steps * W * e);
+  b->tbias = reinterpret_cast<float*>(take((size_t)steps * W * 4));
+  const int shapes[][2] = {{h->W, h->W}, {h->W, h->nqkv}, {h->qd, h->W}, {h->W, 2 * h->M}, {h->M, h->W}, {h->W, h->Apad}};
+  for (const auto& kn : shapes)
+    b->stream_partial_n = std::max(b->stream_partial_n, (size_t)(kn[0] / stream_kb(kn[0])) * R * kn[1]);
+  b->stream_partial = reinterpret_cast<float*>(take(b->stream_partial_n * 4));
+  b->attn_partial_n = attn_partial_floats(h, B, L, 0);
+  b->attn_partial = reinterpret_cast<float*>(take(b->attn_partial_n * 4));
+  b->desc = reinterpret_cast<CallDesc*>(take(sizeof(CallDesc)));
+  b->rope_cs = reinterpret_cast<float2*>(take(R * (h->dh / 2) * sizeof(float2)));
+  return off;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -971,6 +1106,7 @@ pi0x_status upload_weights(pi0x_expert* h, const float* blob, bool head) {
 pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_expert* h) {
   h->cfg = *cfg;
   PI0X_HIP(hipGetDevice(&h->device));
+  scratch_lookup(h->device);
   h->esz = cfg->dtype == PI0X_BF16 ? 2 : 4;
   h->W = cfg->width; h->D = cfg->depth; h->M = cfg->mlp_dim; h->nh = cfg->num_heads; h->dh = cfg->head_dim;
   h->H = cfg->action_horizon; h->A = cfg->action_dim; h->Sd = cfg->state_dim; h->S = h->H + 1;
@@ -1001,7 +1137,8 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
     for (const auto& kn : shapes) h->stream_partial_n = std::max(h->stream_partial_n, stream_partial_floats(kn[0], kn[1]));
     PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
   }
-  PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
+  h->attn_partial_n = (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512;
+  PI0X_TRY(h->allocT(&h->attn_partial, h->attn_partial_n * 4));
   if (h->bf16()) PI0X_TRY(h->allocT(&h->split_partial, kSplitPartialFloats * 4));
   if (!h->bf16()) {
     PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
@@ -1087,7 +1224,8 @@ pi0x_status create_prefix_impl(const pi0x_config* cfg, const void* weights_host,
     for (const auto& kn : shapes) h->stream_partial_n = std::max(h->stream_partial_n, stream_partial_floats(kn[0], kn[1]));
     PI0X_TRY(h->allocT(&h->stream_partial, h->stream_partial_n * 4));
   }
-  PI0X_TRY(h->allocT(&h->attn_partial, (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512 * 4));
+  h->attn_partial_n = (size_t)kAttnPartialBlocks * (2 + h->dh / 4) * 512;
+  PI0X_TRY(h->allocT(&h->attn_partial, h->attn_partial_n * 4));
   if (h->bf16()) PI0X_TRY(h->allocT(&h->split_partial, kSplitPartialFloats * 4));
   if (!h->bf16()) {
     PI0X_TRY(h->allocT(&h->gemm_partial, kGemmPartialFloats * 4));
@@ -1205,6 +1343,45 @@ pi0x_status pi0x_denoise(pi0x_expert* h, int32_t batch, int32_t prefix_len, cons
                          float* actions_out, hipStream_t stream) {
   return pi0x_denoise_ex(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, noise, num_steps, nullptr,
                          actions_out, stream);
+}
+
+pi0x_status pi0x_denoise_noalloc(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                                 const int32_t* prefix_valid_len, const float* state, const float* noise,
+                                 int32_t num_steps, float* actions_out, hipStream_t stream) {
+  PI0X_TRY(check_call(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, noise, actions_out));
+  if (num_steps < 1) return fail(PI0X_ERR_INVALID_ARG, "num_steps must be >= 1");
+  if (num_steps > h->cfg.max_steps) return fail(PI0X_ERR_CAPACITY, "num_steps exceeds max_steps");
+  if (!h->bf16()) return fail(PI0X_ERR_DTYPE, "pi0x_denoise_noalloc needs a bf16 handle");
+  if ((long)batch * h->S > kSmallRows)
+    return fail(PI0X_ERR_CAPACITY, "pi0x_denoise_noalloc takes at most " + std::to_string(kSmallRows) +
+                                       " suffix rows (batch * (action_horizon + 1)), got " +
+                                       std::to_string((long)batch * h->S));
+  CallBufs mine;
+  const size_t need = carve_call_bufs(h, batch, prefix_len, num_steps, nullptr, &mine);
+  if (need > kNoAllocScratchBytes)
+    return fail(PI0X_ERR_CAPACITY, "the call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                       std::to_string(kNoAllocScratchBytes) + " of PI0X_NOALLOC_SCRATCH_BYTES");
+  void* base = nullptr;
+  PI0X_TRY(scratch_of(h->device, &base));
+  carve_call_bufs(h, batch, prefix_len, num_steps, static_cast<char*>(base), &mine);
+  // the suffix values' columns >= S stand for keys that are never visible and
+  // must hold zeros, whatever the previous call left in the array
+  const size_t vts_words = (size_t)batch * h->dh * h->Sp * h->esz / 4;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)std::min<size_t>((vts_words + 255) / 256, 1024)), dim3(256), 0,
+                     stream, reinterpret_cast<uint32_t*>(mine.vts), vts_words);
+  PI0X_HIP(hipGetLastError());
+  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, stream, mine.desc, prefix_kv, prefix_valid_len, state, noise,
+                     actions_out, 0.f, nullptr, nullptr);
+  PI0X_HIP(hipGetLastError());
+  // the handle's buffers are swapped for the carved ones during the enqueue
+  const CallBufs saved = bufs_of(h);
+  const bool timing = h->timing;
+  set_bufs(h, mine);
+  h->timing = false;
+  const pi0x_status st = enqueue<bf16>(h, stream, batch, prefix_len, num_steps, LoopOpts{});
+  set_bufs(h, saved);
+  h->timing = timing;
+  return st;
 }
 
 pi0x_status pi0x_denoise_ex(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
