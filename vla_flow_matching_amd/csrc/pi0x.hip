@@ -151,7 +151,12 @@ struct pi0x_expert {
   CallDesc* desc = nullptr;
   NormDev* norm = nullptr;  // boundary normalization statistics (all modes 0 at create)
   hipStream_t cap_stream = nullptr;
-  std::map<Key, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
+  struct Graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;  // recorded after each replay: the graph is idle once it completes
+  };
+  std::map<Key, Graph> graphs;
   std::vector<Key> graph_order;
   // kernel timing (pi0x_set_timing): event pairs recorded around launches
   bool timing = false;
@@ -685,14 +690,15 @@ pi0x_status run_graph(pi0x_expert* h, const Key& key, F launch_eager, hipStream_
   auto it = h->graphs.find(key);
   if (it == h->graphs.end()) {
     if ((int)h->graphs.size() >= kMaxGraphs) {
-      // the oldest graph may still be replaying from an earlier call: let the
-      // device drain before its executable is destroyed
-      PI0X_HIP(hipDeviceSynchronize());
+      // the oldest graph may still be replaying from an earlier call: wait
+      // for its last replay only (not the whole device) before destroying it
       const Key old = h->graph_order.front();
       h->graph_order.erase(h->graph_order.begin());
       auto o = h->graphs.find(old);
-      (void)hipGraphExecDestroy(o->second.second);
-      (void)hipGraphDestroy(o->second.first);
+      PI0X_HIP(hipEventSynchronize(o->second.done));
+      (void)hipGraphExecDestroy(o->second.exec);
+      (void)hipGraphDestroy(o->second.graph);
+      (void)hipEventDestroy(o->second.done);
       h->graphs.erase(o);
     }
     PI0X_HIP(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
@@ -710,10 +716,18 @@ pi0x_status run_graph(pi0x_expert* h, const Key& key, F launch_eager, hipStream_
       (void)hipGraphDestroy(graph);
       return fail(PI0X_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
     }
-    it = h->graphs.emplace(key, std::make_pair(graph, exec)).first;
+    hipEvent_t done = nullptr;
+    e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipGraphExecDestroy(exec);
+      (void)hipGraphDestroy(graph);
+      return fail(PI0X_ERR_HIP, std::string("hipEventCreateWithFlags: ") + hipGetErrorString(e));
+    }
+    it = h->graphs.emplace(key, pi0x_expert::Graph{graph, exec, done}).first;
     h->graph_order.push_back(key);
   }
-  PI0X_HIP(hipGraphLaunch(it->second.second, stream));
+  PI0X_HIP(hipGraphLaunch(it->second.exec, stream));
+  PI0X_HIP(hipEventRecord(it->second.done, stream));
   return PI0X_OK;
 }
 
@@ -1253,8 +1267,9 @@ pi0x_status create_prefix_impl(const pi0x_config* cfg, const void* weights_host,
 void destroy_impl(pi0x_expert* h) {
   (void)hipDeviceSynchronize();
   for (auto& kv : h->graphs) {
-    (void)hipGraphExecDestroy(kv.second.second);
-    (void)hipGraphDestroy(kv.second.first);
+    (void)hipGraphExecDestroy(kv.second.exec);
+    (void)hipGraphDestroy(kv.second.graph);
+    (void)hipEventDestroy(kv.second.done);
   }
   h->graphs.clear();
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
