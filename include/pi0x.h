@@ -265,6 +265,16 @@ pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable);
 pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches);
 
 /*
+ * Guard check, a debugging aid.  Every device buffer a handle allocates is
+ * followed by a 4 KiB guard filled with the byte 0xA5 at creation; this
+ * synchronises the device and sets *corrupted to the number of guards that
+ * no longer hold the pattern, i.e. buffers some kernel wrote past.  0 is the
+ * only correct result.  Errors: PI0X_ERR_INVALID_ARG for NULL arguments,
+ * PI0X_ERR_HIP if a copy fails.
+ */
+pi0x_status pi0x_expert_check_guards(pi0x_expert* h, int32_t* corrupted);
+
+/*
  * The prefix pass (page 1: sample_actions builds the prefix masks and
  * positions and runs the prefix-only branch of
  * PaliGemmaWithExpertModel.forward, _compute_layer_prefix_only per layer),
@@ -329,6 +339,8 @@ void pi0x_prefix_destroy(pi0x_prefix_model* p);
 /* Kernel timing of the prefix pass, as pi0x_set_timing / pi0x_read_timing. */
 pi0x_status pi0x_prefix_set_timing(pi0x_prefix_model* p, int32_t enable);
 pi0x_status pi0x_prefix_read_timing(pi0x_prefix_model* p, double* total_ms, int64_t* launches);
+/* pi0x_expert_check_guards for the prefix-pass handle. */
+pi0x_status pi0x_prefix_check_guards(pi0x_prefix_model* p, int32_t* corrupted);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,5 @@
 import os
+import pytest
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -8,3 +9,31 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+# Every handle a test closes must still hold the 0xA5 guards its creation put
+# after each of its device buffers: a kernel that wrote past a buffer fails
+# the test that closes the handle.
+@pytest.fixture(autouse=True, scope="session")
+def _handles_close_with_intact_guards():
+    try:
+        from vla_flow_matching_amd import binding
+    except Exception:  # the library is not importable: nothing to wrap
+        yield
+        return
+    saved = {}
+    for cls in (binding.Expert, binding.PrefixModel):
+        saved[cls] = cls.close
+
+        def close(self, _orig=cls.close):
+            if getattr(self, "h", 0):
+                bad = self.guard_violations()
+                if bad:
+                    _orig(self)
+                    raise AssertionError(f"{bad} device buffer(s) of the handle were written past their end")
+            _orig(self)
+
+        cls.close = close
+    yield
+    for cls, fn in saved.items():
+        cls.close = fn

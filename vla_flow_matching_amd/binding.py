@@ -118,6 +118,10 @@ def lib() -> ctypes.CDLL:
         L.pi0x_prefix_set_timing.restype = i32
         L.pi0x_prefix_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.pi0x_prefix_read_timing.restype = i32
+        L.pi0x_expert_check_guards.argtypes = [vp, ctypes.POINTER(i32)]
+        L.pi0x_expert_check_guards.restype = i32
+        L.pi0x_prefix_check_guards.argtypes = [vp, ctypes.POINTER(i32)]
+        L.pi0x_prefix_check_guards.restype = i32
         _lib = L
     return _lib
 
@@ -239,6 +243,18 @@ def pi0x_read_timing(h) -> tuple[int, dict]:
     cnt = (ctypes.c_int64 * n)()
     st = lib().pi0x_read_timing(h, ms, cnt)
     return st, {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+
+def pi0x_expert_check_guards(h) -> tuple[int, int]:
+    n = ctypes.c_int32(0)
+    st = lib().pi0x_expert_check_guards(h, ctypes.byref(n))
+    return st, n.value
+
+
+def pi0x_prefix_check_guards(p) -> tuple[int, int]:
+    n = ctypes.c_int32(0)
+    st = lib().pi0x_prefix_check_guards(p, ctypes.byref(n))
+    return st, n.value
 
 
 def check(status: int) -> None:
@@ -383,6 +399,12 @@ class Expert:
                                 self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
         return out
 
+    def guard_violations(self) -> int:
+        """Buffers of the handle that a kernel wrote past (0 is correct)."""
+        st, n = pi0x_expert_check_guards(self.h)
+        check(st)
+        return n
+
     def set_normalization(self, state: dict | None = None, action: dict | None = None):
         """State / action statistics in the page's format (see norm_struct); None turns a side off."""
         check(pi0x_set_normalization(self.h, state, action))
@@ -454,6 +476,12 @@ class PrefixModel:
     def _stream(self, stream):
         import torch
         return (stream or torch.cuda.current_stream()).cuda_stream
+
+    def guard_violations(self) -> int:
+        """Buffers of the handle that a kernel wrote past (0 is correct)."""
+        st, n = pi0x_prefix_check_guards(self.h)
+        check(st)
+        return n
 
     def set_timing(self, enable: bool):
         check(pi0x_prefix_set_timing(self.h, enable))

@@ -46,6 +46,7 @@
 #include <vector>
 
 #include "attention.h"
+#include "host_pack.h"
 #include "common.h"
 #include "gemm.h"
 #include "small_kernels.h"
@@ -108,14 +109,6 @@ struct Key {
   }
 };
 
-uint16_t host_bf16(float f) {
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 }  // namespace
@@ -166,15 +159,26 @@ struct pi0x_expert {
 
   bool bf16() const { return cfg.dtype == PI0X_BF16; }
 
+  // Every buffer is followed by a guard of kGuardBytes holding kGuardByte
+  // (set here, at creation); pi0x_expert_check_guards counts the guards a
+  // kernel has written into.
+  static constexpr size_t kGuardBytes = 4096;
+  static constexpr int kGuardByte = 0xA5;
+  std::vector<unsigned char*> guards;
   pi0x_status alloc(void** p, size_t bytes) {
     *p = nullptr;
     if (bytes == 0) bytes = 256;
-    hipError_t e = hipMalloc(p, bytes);
+    const size_t body = (bytes + 255) / 256 * 256;
+    hipError_t e = hipMalloc(p, body + kGuardBytes);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return fail(PI0X_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
     }
     allocs.push_back(*p);
+    unsigned char* g = static_cast<unsigned char*>(*p) + body;
+    e = hipMemset(g, kGuardByte, kGuardBytes);
+    if (e != hipSuccess) return fail(PI0X_ERR_HIP, std::string("hipMemset of a guard: ") + hipGetErrorString(e));
+    guards.push_back(g);
     return PI0X_OK;
   }
   template <typename P>
@@ -934,186 +938,54 @@ pi0x_status run_prefix(pi0x_expert* h, int B, int L, hipStream_t stream) {
 }
 
 pi0x_status check_config(const pi0x_config* c) {
-  if (!c) return fail(PI0X_ERR_INVALID_ARG, "config is NULL");
-  if (c->width <= 0 || c->depth <= 0 || c->mlp_dim <= 0 || c->num_heads <= 0 || c->num_kv_heads <= 0 ||
-      c->head_dim <= 0 || c->action_horizon <= 0 || c->action_dim <= 0 || c->state_dim <= 0 || c->max_batch <= 0 ||
-      c->max_prefix_len < 0 || c->max_steps <= 0)
-    return fail(PI0X_ERR_INVALID_ARG, "config has a non-positive dimension or capacity");
-  if (c->dtype != PI0X_FP32 && c->dtype != PI0X_BF16) return fail(PI0X_ERR_DTYPE, "unknown dtype");
-  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->time_min_period > 0.f) || !(c->time_max_period > 0.f))
-    return fail(PI0X_ERR_INVALID_ARG, "config has an invalid rms_eps, rope_theta or time period");
-  if (c->num_kv_heads != 1) return fail(PI0X_ERR_SHAPE, "only num_kv_heads == 1 is supported");
-  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
-    return fail(PI0X_ERR_SHAPE, "head_dim must be 32, 64, 128 or 256");
-  if (c->width % 256 != 0) return fail(PI0X_ERR_SHAPE, "width must be a multiple of 256");
-  if (c->mlp_dim % 128 != 0) return fail(PI0X_ERR_SHAPE, "mlp_dim must be a multiple of 128");
-  if ((c->num_heads * c->head_dim) % 128 != 0)
-    return fail(PI0X_ERR_SHAPE, "num_heads*head_dim must be a multiple of 128");
-  if (c->action_dim > 64 || c->state_dim > 64) return fail(PI0X_ERR_SHAPE, "action_dim and state_dim must be <= 64");
-  if ((long)c->max_batch * (c->action_horizon + 1) > (1L << 24)) return fail(PI0X_ERR_CAPACITY, "max_batch too large");
-  return PI0X_OK;
+  std::string msg;
+  const pi0x_status st = hostpack::config_error(c, &msg);
+  return st == PI0X_OK ? PI0X_OK : fail(st, msg);
 }
 
-size_t weight_count(const pi0x_config* c) {
-  const size_t W = c->width, M = c->mlp_dim, qd = (size_t)c->num_heads * c->head_dim,
-               kd = (size_t)c->num_kv_heads * c->head_dim;
-  const size_t A = c->action_dim, Sd = c->state_dim;
-  const size_t layer = W + qd * W + 2 * kd * W + W * qd + W + 3 * M * W;
-  return layer * c->depth + W + (W * Sd + W) + (W * A + W) + (W * 2 * W + W) + (W * W + W) + (A * W + A);
-}
+size_t weight_count(const pi0x_config* c) { return hostpack::weight_count(c); }
 
-template <typename E>
-void put(std::vector<E>& dst, size_t i, float v);
-template <>
-void put<float>(std::vector<float>& dst, size_t i, float v) { dst[i] = v; }
-template <>
-void put<uint16_t>(std::vector<uint16_t>& dst, size_t i, float v) { dst[i] = host_bf16(v); }
-
-// head == false: a prefix-pass blob (decoder layers only).
+// Repacks the blob (host_pack.h) and uploads it.  head == false: a
+// prefix-pass blob (decoder layers only).
 template <typename E>
 pi0x_status upload_weights(pi0x_expert* h, const float* blob, bool head) {
-  const int W = h->W, M = h->M, qd = h->qd, dh = h->dh, half = dh / 2;
-  const size_t layer_sz = (size_t)W + (size_t)qd * W + 2 * (size_t)dh * W + (size_t)W * qd + W + 3 * (size_t)M * W;
+  const hostpack::Dims d{h->W, h->M, h->nh, h->dh, h->A, h->Sd, h->bf16()};
   auto up = [&](void** dst, const std::vector<E>& v) -> pi0x_status {
     PI0X_TRY(h->alloc(dst, v.size() * sizeof(E)));
     PI0X_HIP(hipMemcpy(*dst, v.data(), v.size() * sizeof(E), hipMemcpyHostToDevice));
     return PI0X_OK;
   };
-  // value in the model dtype, as float (bf16 mode: the blob value rounded to bf16)
-  auto md = [&](float x) -> float {
-    if (!h->bf16()) return x;
-    uint32_t u = (uint32_t)host_bf16(x) << 16;
-    float r;
-    std::memcpy(&r, &u, 4);
-    return r;
+  auto up_f32 = [&](float** dst, const std::vector<float>& v) -> pi0x_status {
+    PI0X_TRY(h->allocT(dst, v.size() * sizeof(float)));
+    PI0X_HIP(hipMemcpy(*dst, v.data(), v.size() * sizeof(float), hipMemcpyHostToDevice));
+    return PI0X_OK;
   };
   h->layers.resize(h->D);
   for (int l = 0; l < h->D; ++l) {
-    const float* p = blob + (size_t)l * layer_sz;
-    const float* in_norm = p;
-    const float* wq = in_norm + W;
-    const float* wk = wq + (size_t)qd * W;
-    const float* wv = wk + (size_t)dh * W;
-    const float* wo = wv + (size_t)dh * W;
-    const float* post = wo + (size_t)W * qd;
-    const float* wg = post + W;
-    const float* wu = wg + (size_t)M * W;
-    const float* wd = wu + (size_t)M * W;
+    const hostpack::LayerSrc src = hostpack::layer_src(blob, d, l);
     Layer& ly = h->layers[l];
-    std::vector<float> s_in(W), s_post(W);
-    for (int k = 0; k < W; ++k) {
-      s_in[k] = 1.0f + md(in_norm[k]);
-      s_post[k] = 1.0f + md(post[k]);
-    }
-    {
-      const int rows = qd + 2 * dh;
-      std::vector<E> v((size_t)rows * W);
-      for (int c = 0; c < rows; ++c) {
-        const float* src;
-        if (c < qd + dh) {
-          const int head = c / dh, w = c % dh;
-          const int orig = ((w % 32) / 16) * half + (w / 32) * 16 + (w % 16);
-          src = head < h->nh ? wq + ((size_t)head * dh + orig) * W : wk + (size_t)orig * W;
-        } else {
-          src = wv + (size_t)(c - qd - dh) * W;
-        }
-        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, md(src[k]) * s_in[k]);
-      }
-      PI0X_TRY(up(&ly.wqkv, v));
-    }
-    {
-      std::vector<E> v((size_t)W * qd);
-      for (size_t i = 0; i < v.size(); ++i) put<E>(v, i, wo[i]);
-      PI0X_TRY(up(&ly.wo, v));
-    }
-    {
-      std::vector<E> v((size_t)2 * M * W);
-      for (int c = 0; c < 2 * M; ++c) {
-        const int pblk = c / 32, sel = (c % 32) / 16, e = c % 16;
-        const float* src = (sel == 0 ? wg : wu) + ((size_t)pblk * 16 + e) * W;
-        for (int k = 0; k < W; ++k) put<E>(v, (size_t)c * W + k, md(src[k]) * s_post[k]);
-      }
-      PI0X_TRY(up(&ly.wgu, v));
-    }
-    {
-      std::vector<E> v((size_t)W * M);
-      for (size_t i = 0; i < v.size(); ++i) put<E>(v, i, wd[i]);
-      PI0X_TRY(up(&ly.wdown, v));
-    }
+    PI0X_TRY(up(&ly.wqkv, hostpack::pack_qkv<E>(src, d)));
+    PI0X_TRY(up(&ly.wo, hostpack::pack_plain<E>(src.wo, (size_t)h->W * h->qd)));
+    PI0X_TRY(up(&ly.wgu, hostpack::pack_gate_up<E>(src, d)));
+    PI0X_TRY(up(&ly.wdown, hostpack::pack_plain<E>(src.wd, (size_t)h->W * h->M)));
   }
   if (!head) return PI0X_OK;
-  const float* p = blob + (size_t)h->D * layer_sz;
-  const float* final_norm = p;
-  const float* ws = final_norm + W;
-  const float* bs = ws + (size_t)W * h->Sd;
-  const float* wi = bs + W;
-  const float* bi = wi + (size_t)W * h->A;
-  const float* wmi = bi + W;
-  const float* bmi = wmi + (size_t)W * 2 * W;
-  const float* wmo = bmi + W;
-  const float* bmo = wmo + (size_t)W * W;
-  const float* wout = bmo + W;
-  const float* bout = wout + (size_t)h->A * W;
-  const int A = h->A;
+  const hostpack::HeadSrc hs = hostpack::head_src(blob, d, h->D);
+  PI0X_TRY(up(&h->w_tt, hostpack::pack_time_half<E>(hs, d)));
+  PI0X_TRY(up(&h->w_mo, hostpack::pack_plain<E>(hs.wmo, (size_t)h->W * h->W)));
   {
-    std::vector<E> vt((size_t)W * W), vo((size_t)W * W);
-    for (int r = 0; r < W; ++r)
-      for (int k = 0; k < W; ++k) {
-        put<E>(vt, (size_t)r * W + k, wmi[(size_t)r * 2 * W + W + k]);
-        put<E>(vo, (size_t)r * W + k, wmo[(size_t)r * W + k]);
-      }
-    PI0X_TRY(up(&h->w_tt, vt));
-    PI0X_TRY(up(&h->w_mo, vo));
+    std::vector<float> comb, bias;
+    hostpack::fold_action_in(hs, d, &comb, &bias);
+    PI0X_TRY(up_f32(&h->w_comb, comb));
+    PI0X_TRY(up_f32(&h->b_mi, bias));
   }
-  // action_in_proj folded into the action half of action_time_mlp_in:
-  // W_mi,a (W_in x + b_in) = (W_mi,a W_in) x + W_mi,a b_in, products in double
-  {
-    std::vector<float> comb((size_t)W * A), bmi2(W);
-    std::vector<double> win((size_t)W * A), bin(W);
-    for (size_t i = 0; i < win.size(); ++i) win[i] = md(wi[i]);
-    for (int k = 0; k < W; ++k) bin[k] = md(bi[k]);
-    std::vector<double> acc(A);
-    for (int o = 0; o < W; ++o) {
-      std::fill(acc.begin(), acc.end(), 0.0);
-      double bacc = md(bmi[o]);
-      const float* wr = wmi + (size_t)o * 2 * W;
-      for (int k = 0; k < W; ++k) {
-        const double wk = md(wr[k]);
-        const double* wik = &win[(size_t)k * A];
-        for (int a = 0; a < A; ++a) acc[a] += wk * wik[a];
-        bacc += wk * bin[k];
-      }
-      for (int a = 0; a < A; ++a) comb[(size_t)a * W + o] = (float)acc[a];
-      bmi2[o] = (float)bacc;
-    }
-    PI0X_TRY(h->allocT(&h->w_comb, comb.size() * sizeof(float)));
-    PI0X_HIP(hipMemcpy(h->w_comb, comb.data(), comb.size() * sizeof(float), hipMemcpyHostToDevice));
-    PI0X_TRY(h->allocT(&h->b_mi, W * sizeof(float)));
-    PI0X_HIP(hipMemcpy(h->b_mi, bmi2.data(), W * sizeof(float), hipMemcpyHostToDevice));
-  }
-  // action_out_proj with the final norm's (1 + w) folded into its columns,
-  // padded with zero rows to a multiple of 128 outputs
-  {
-    h->Apad = round_up(A, 128);
-    std::vector<E> v((size_t)h->Apad * W);
-    for (int r = 0; r < h->Apad; ++r)
-      for (int k = 0; k < W; ++k)
-        put<E>(v, (size_t)r * W + k, r < A ? md(wout[(size_t)r * W + k]) * (1.0f + md(final_norm[k])) : 0.f);
-    PI0X_TRY(up(&h->w_outp, v));
-  }
-  // state_proj and the remaining biases stay float32 (bf16 mode: the blob's
-  // values rounded to bf16, held exactly in float32)
-  auto small = [&](float** dst, const float* src, size_t n) -> pi0x_status {
-    std::vector<float> v(n);
-    for (size_t i = 0; i < n; ++i) v[i] = md(src[i]);
-    PI0X_TRY(h->allocT(dst, n * sizeof(float)));
-    PI0X_HIP(hipMemcpy(*dst, v.data(), n * sizeof(float), hipMemcpyHostToDevice));
-    return PI0X_OK;
-  };
-  PI0X_TRY(small(&h->b_mo, bmo, W));
-  PI0X_TRY(small(&h->w_s, ws, (size_t)W * h->Sd));
-  PI0X_TRY(small(&h->b_s, bs, W));
-  PI0X_TRY(small(&h->b_out, bout, A));
+  h->Apad = round_up(h->A, 128);
+  PI0X_TRY(up(&h->w_outp, hostpack::pack_out_proj<E>(hs, d, h->Apad)));
+  // state_proj and the remaining biases stay float32
+  PI0X_TRY(up_f32(&h->b_mo, hostpack::pack_small(hs.bmo, h->W, d.bf16)));
+  PI0X_TRY(up_f32(&h->w_s, hostpack::pack_small(hs.ws, (size_t)h->W * h->Sd, d.bf16)));
+  PI0X_TRY(up_f32(&h->b_s, hostpack::pack_small(hs.bs, h->W, d.bf16)));
+  PI0X_TRY(up_f32(&h->b_out, hostpack::pack_small(hs.bout, h->A, d.bf16)));
   return PI0X_OK;
 }
 
@@ -1187,25 +1059,12 @@ pi0x_status create_impl(const pi0x_config* cfg, const void* weights_host, pi0x_e
 constexpr long kMaxPrefixRows = 1L << 16;
 
 pi0x_status check_prefix_config(const pi0x_config* c) {
-  if (!c) return fail(PI0X_ERR_INVALID_ARG, "config is NULL");
-  pi0x_config k = *c;  // the action-head fields do not apply to the prefix pass
-  k.action_horizon = 1;
-  k.action_dim = 1;
-  k.state_dim = 1;
-  k.max_steps = 1;
-  k.time_min_period = k.time_max_period = 1.f;
-  PI0X_TRY(check_config(&k));
-  if (c->max_prefix_len < 1) return fail(PI0X_ERR_INVALID_ARG, "max_prefix_len must be >= 1");
-  if ((long)c->max_batch * c->max_prefix_len > kMaxPrefixRows)
-    return fail(PI0X_ERR_CAPACITY, "max_batch * max_prefix_len exceeds 65536 rows");
-  return PI0X_OK;
+  std::string msg;
+  const pi0x_status st = hostpack::prefix_config_error(c, kMaxPrefixRows, &msg);
+  return st == PI0X_OK ? PI0X_OK : fail(st, msg);
 }
 
-size_t prefix_weight_count(const pi0x_config* c) {
-  const size_t W = c->width, M = c->mlp_dim, qd = (size_t)c->num_heads * c->head_dim,
-               kd = (size_t)c->num_kv_heads * c->head_dim;
-  return (W + qd * W + 2 * kd * W + W * qd + W + 3 * M * W) * c->depth;
-}
+size_t prefix_weight_count(const pi0x_config* c) { return hostpack::prefix_weight_count(c); }
 
 pi0x_status create_prefix_impl(const pi0x_config* cfg, const void* weights_host, pi0x_expert* h) {
   h->cfg = *cfg;
@@ -1552,6 +1411,27 @@ void pi0x_prefix_destroy(pi0x_prefix_model* p) {
   if (!p) return;
   destroy_impl(&p->core);
   delete p;
+}
+
+pi0x_status pi0x_expert_check_guards(pi0x_expert* h, int32_t* corrupted) {
+  if (!h || !corrupted) return fail(PI0X_ERR_INVALID_ARG, "a pointer argument is NULL");
+  *corrupted = 0;
+  PI0X_HIP(hipDeviceSynchronize());
+  std::vector<unsigned char> host(pi0x_expert::kGuardBytes);
+  for (unsigned char* g : h->guards) {
+    PI0X_HIP(hipMemcpy(host.data(), g, host.size(), hipMemcpyDeviceToHost));
+    for (unsigned char b : host)
+      if (b != (unsigned char)pi0x_expert::kGuardByte) {
+        ++*corrupted;
+        break;
+      }
+  }
+  return PI0X_OK;
+}
+
+pi0x_status pi0x_prefix_check_guards(pi0x_prefix_model* p, int32_t* corrupted) {
+  if (!p) return fail(PI0X_ERR_INVALID_ARG, "handle is NULL");
+  return pi0x_expert_check_guards(&p->core, corrupted);
 }
 
 pi0x_status pi0x_prefix_set_timing(pi0x_prefix_model* p, int32_t enable) {
