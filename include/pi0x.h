@@ -265,6 +265,51 @@ pi0x_status pi0x_set_timing(pi0x_expert* h, int32_t enable);
 pi0x_status pi0x_read_timing(pi0x_expert* h, double* total_ms, int64_t* launches);
 
 /*
+ * Test-only stage read-out, for per-kernel parity tests.  Runs the single
+ * velocity evaluation of pi0x_denoise_step (page 1, denoise_step: embed_suffix,
+ * then per expert layer of _compute_layer_suffix_only the normed q/k/v
+ * projection with RoPE, _attend over the prefix cache and the suffix, o_proj
+ * plus the residual, the normed gate/up projection with GeGLU, down plus the
+ * residual) eagerly on `stream`, stops after `stage` of layer `layer` (the
+ * layer is ignored for PI0X_DEBUG_AFTER_EMBED) and copies one of the handle's
+ * working buffers, as it stands at that point, to dst (device memory, at
+ * least the buffer's size; the copy is ordered on `stream`):
+ *   PI0X_DEBUG_RESIDUAL  float32 [batch*S][width], S = horizon + 1: the
+ *                        residual stream (row 0 of a sample is its state token)
+ *   PI0X_DEBUG_QK        model dtype [batch*S][qd + head_dim]: the queries
+ *                        (heads in order) then the key, after RoPE
+ *   PI0X_DEBUG_VT        model dtype [batch][head_dim][Sp], Sp = S rounded up
+ *                        to 64: the suffix values, transposed; key
+ *                        s = 32a + 16b + 4c + d sits at column
+ *                        32a + 8c + 4b + d (columns of keys >= S hold 0)
+ *   PI0X_DEBUG_ATTN_OUT  model dtype [batch*S][qd]: attention output, heads in order
+ *   PI0X_DEBUG_GEGLU     model dtype [batch*S][mlp_dim]: gelu_tanh(gate) * up
+ * Arguments as pi0x_denoise_step (x_t, t); nothing is written to any output
+ * of the call.  Errors as pi0x_denoise_step, plus PI0X_ERR_INVALID_ARG for an
+ * unknown stage or buffer or a layer out of range and PI0X_ERR_CAPACITY for
+ * a short dst.
+ */
+typedef enum {
+  PI0X_DEBUG_AFTER_EMBED = 0,
+  PI0X_DEBUG_AFTER_QKV = 1,
+  PI0X_DEBUG_AFTER_ATTENTION = 2,
+  PI0X_DEBUG_AFTER_O_PROJ = 3,
+  PI0X_DEBUG_AFTER_GATE_UP = 4,
+  PI0X_DEBUG_AFTER_DOWN = 5
+} pi0x_debug_stage;
+typedef enum {
+  PI0X_DEBUG_RESIDUAL = 0,
+  PI0X_DEBUG_QK = 1,
+  PI0X_DEBUG_VT = 2,
+  PI0X_DEBUG_ATTN_OUT = 3,
+  PI0X_DEBUG_GEGLU = 4
+} pi0x_debug_buffer;
+pi0x_status pi0x_debug_velocity_until(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                                      const int32_t* prefix_valid_len, const float* state, const float* x_t, float t,
+                                      int32_t stage, int32_t layer, int32_t buffer, void* dst, size_t dst_bytes,
+                                      hipStream_t stream);
+
+/*
  * Guard check, a debugging aid.  Every device buffer a handle allocates is
  * followed by a 4 KiB guard filled with the byte 0xA5 at creation; this
  * synchronises the device and sets *corrupted to the number of guards that

@@ -210,6 +210,86 @@ class Oracle:
                                   int(valid), _p(pos), int(bool(causal)))
         return h
 
+    # --- single stages, for per-kernel tests ------------------------------
+    # One expert layer of page 1's _compute_layer_suffix_only split where the
+    # library's kernels split it, each stage composed from the oracle's own
+    # primitives (rmsnorm, rope, attend_one, gelu_tanh) and matrix products in
+    # the order the page states; chained they give layer() (pinned in
+    # tests/test_oracle_pins.py).  Rows are the suffix tokens of one sample.
+
+    def layer_weights(self, l: int) -> dict:
+        """Layer l's tensors in the blob's order: input norm, q, k, v, o, post
+        norm, gate, up, down (matrices [out][in])."""
+        s = self.shape
+        W, M, dh = s.width, s.mlp_dim, s.head_dim
+        qd, kd = s.num_heads * dh, s.num_kv_heads * dh
+        size = (self.w.size - self._head_size()) // s.depth
+        blob = self.w[l * size:(l + 1) * size]
+        out, p = {}, 0
+        for name, shp in [("in_norm", (W,)), ("wq", (qd, W)), ("wk", (kd, W)), ("wv", (kd, W)), ("wo", (W, qd)),
+                          ("post_norm", (W,)), ("wgate", (M, W)), ("wup", (M, W)), ("wdown", (W, M))]:
+            n = int(np.prod(shp))
+            out[name] = blob[p:p + n].reshape(shp)
+            p += n
+        return out
+
+    def stage_qkv(self, l: int, h, pos):
+        """input_layernorm, q/k/v projections, rotary embedding of q and k at
+        positions pos[r]: (q [S][qd], k [S][kd], v [S][kd])."""
+        s, lw = self.shape, self.layer_weights(l)
+        h = _f64(h)
+        y = np.stack([rmsnorm(h[r], lw["in_norm"], s.rms_eps) for r in range(h.shape[0])])
+        q, k, v = y @ lw["wq"].T, y @ lw["wk"].T, y @ lw["wv"].T
+        dh = s.head_dim
+        for r in range(h.shape[0]):
+            for n in range(s.num_heads):
+                q[r, n * dh:(n + 1) * dh] = rope(q[r, n * dh:(n + 1) * dh], pos[r], s.rope_theta)
+            for n in range(s.num_kv_heads):
+                k[r, n * dh:(n + 1) * dh] = rope(k[r, n * dh:(n + 1) * dh], pos[r], s.rope_theta)
+        return q, k, v
+
+    def stage_attention(self, q, k, v, kp, vp, valid: int, causal: bool = False):
+        """_attend for every suffix row and query head: prefix keys [0, valid)
+        of the (single) kv head and the suffix keys the mask shows.
+        q [S][qd]; k, v [S][dh]; kp, vp [L][dh].  Returns o [S][qd]."""
+        s = self.shape
+        dh, S = s.head_dim, q.shape[0]
+        o = np.empty((S, s.num_heads * dh))
+        for r in range(S):
+            for n in range(s.num_heads):
+                o[r, n * dh:(n + 1) * dh] = attend_one(q[r, n * dh:(n + 1) * dh], kp, vp, valid, k, v, r,
+                                                       1.0 / np.sqrt(dh), causal)
+        return o
+
+    def stage_o_proj(self, l: int, h, o):
+        """o_proj and the first residual add: h + o W_o^T."""
+        return _f64(h) + _f64(o) @ self.layer_weights(l)["wo"].T
+
+    def stage_gate_up(self, l: int, h):
+        """post_attention_layernorm, then gelu_tanh(gate) * up: [S][mlp_dim]."""
+        s, lw = self.shape, self.layer_weights(l)
+        h = _f64(h)
+        y = np.stack([rmsnorm(h[r], lw["post_norm"], s.rms_eps) for r in range(h.shape[0])])
+        g, u = y @ lw["wgate"].T, y @ lw["wup"].T
+        return np.vectorize(gelu_tanh)(g) * u
+
+    def stage_down(self, l: int, h, g):
+        """down projection and the second residual add: h + g W_down^T."""
+        return _f64(h) + _f64(g) @ self.layer_weights(l)["wdown"].T
+
+    def stage_head(self, h):
+        """The expert's final norm on the action rows (1..H) and action_out_proj:
+        the velocity [H][A] (page 1, denoise_step's last lines)."""
+        s = self.shape
+        W, A, Sd = s.width, s.action_dim, s.state_dim
+        head = self.w[self.w.size - self._head_size():]
+        final_norm = head[:W]
+        tail = head[W + W * Sd + W + W * A + W + W * 2 * W + W + W * W + W:]
+        w_out, b_out = tail[:A * W].reshape(A, W), tail[A * W:]
+        h = _f64(h)
+        y = np.stack([rmsnorm(h[r], final_norm, s.rms_eps) for r in range(1, h.shape[0])])
+        return y @ w_out.T + b_out
+
     def _head_size(self):
         s = self.shape
         W, A, Sd = s.width, s.action_dim, s.state_dim

@@ -19,7 +19,8 @@ def test_library_exports_every_declared_function():
                           "pi0x_read_timing", "pi0x_set_normalization", "pi0x_denoise_ex",
                           "pi0x_prefix_config_default", "pi0x_prefix_weight_count", "pi0x_prefix_create",
                           "pi0x_prefill", "pi0x_prefix_destroy", "pi0x_prefix_set_timing",
-                          "pi0x_prefix_read_timing", "pi0x_expert_check_guards", "pi0x_prefix_check_guards"}
+                          "pi0x_prefix_read_timing", "pi0x_expert_check_guards", "pi0x_prefix_check_guards",
+                          "pi0x_debug_velocity_until"}
     lib = b.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -92,6 +93,7 @@ def test_calls_reject_null_handle():
     assert b.pi0x_set_timing(None, 1) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_read_timing(None)[0] == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_expert_check_guards(None)[0] == b.PI0X_ERR_INVALID_ARG
+    assert b.pi0x_debug_velocity_until(None, 1, 8, 1, 1, 1, 1, 0.5, 1, 0, 0, 1, 64, None) == b.PI0X_ERR_INVALID_ARG
     assert b.pi0x_prefix_check_guards(None)[0] == b.PI0X_ERR_INVALID_ARG
     b.pi0x_expert_destroy(None)  # ignored
 

@@ -1,0 +1,194 @@
+"""Per-kernel parity at the full pi0 expert shape (bf16, batch 1, an 816-key
+prefix): every stage of the velocity evaluation, read out of the library with
+pi0x_debug_velocity_until and compared with the oracle's stage function
+applied to the library's own input of that stage, so a failure names the
+kernel it is in.
+
+Stages (page 1, embed_suffix and _compute_layer_suffix_only):
+suffix embedding; input norm + q/k/v + RoPE; attention over the prefix cache
+and the suffix (valid length 0, all 816 keys, and a ragged 700); o_proj +
+residual; post-attention norm + gate/up + GeGLU; down + residual; and the
+head (final norm + action_out_proj) with the Euler update.
+
+Bar for one stage: relative L2 <= 1e-2 and max|diff| <= 2e-2 * max|ref|.  A
+single stage rounds its inputs and its output to bf16 once (relative 2^-9
+each), and its float32 accumulation over K <= 4096 adds far less, so the
+expected error is a few 1e-3; the bar leaves room for the bf16 exponentials
+and probabilities of attention and for the worst element of a 50k-element
+output."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from vla_flow_matching_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+W1 = synth.WORKLOADS["pi0_bf16_b1"]
+S = W1.shape.suffix_len
+DH = W1.shape.head_dim
+QD = W1.shape.num_heads * DH
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def check_stage(gpu, ref, what, rel_bar=1e-2, max_bar=2e-2):
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    d = np.abs(gpu - ref)
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    mx = float(d.max() / max(np.abs(ref).max(), 1e-30))
+    _say(f"{what}: rel-L2 {rel:.3e} max|diff|/max|ref| {mx:.3e}")
+    assert rel <= rel_bar and mx <= max_bar, f"{what}: rel-L2 {rel} scaled max {mx}"
+
+
+def _vt_column(s):
+    # the transposed suffix values put key s = 32a + 16b + 4c + d at column
+    # 32a + 8c + 4b + d (the order attention's fragments read them in)
+    s = np.asarray(s)
+    return (s & ~31) | (((s >> 2) & 3) << 3) | (((s >> 4) & 1) << 2) | (s & 3)
+
+
+class Stages:
+    def __init__(self, seed=51):
+        from vla_flow_matching_amd import binding
+        self.w = W1.replace(name=f"pi0_bf16_b1_stages_s{seed}", seed=seed)
+        # nonzero norm weights, so the (1 + w) folds are exercised
+        self.blob = synth.make_weights(self.w.shape, seed=seed, dtype="bf16", norm_std=0.1)
+        self.inputs = synth.make_inputs(self.w)
+        cfg = binding.make_config(self.w.shape, "bf16", max_batch=1, max_prefix_len=1024, max_steps=4)
+        _say(f"create pi0 bf16 B=1 (stages) seed={seed}")
+        self.ex = binding.Expert(cfg, self.blob)
+        self.dev = binding.device_inputs(self.inputs, "bf16")
+        self.orc = oracle.Oracle(self.w.shape, self.blob)
+        rng = np.random.default_rng(seed)
+        self.x = rng.standard_normal((1, W1.shape.horizon, W1.shape.action_dim)).astype(np.float32)
+        self.x_dev = torch.from_numpy(self.x).cuda()
+        self.t = float(np.float32(0.7))
+
+    def valid_dev(self, v):
+        return torch.full((1,), v, dtype=torch.int32, device="cuda")
+
+    def read(self, valid, stage, layer, buffer):
+        _say(f"debug read valid={valid} stage={stage} layer={layer} buffer={buffer}")
+        out = self.ex.debug_until(self.dev["prefix_kv"], self.valid_dev(valid), self.dev["state"], self.x_dev,
+                                  self.t, stage, layer, buffer)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64)
+
+    def residual_before(self, valid, l):
+        if l == 0:
+            return self.read(valid, "embed", 0, "residual").reshape(S, -1)
+        return self.read(valid, "down", l - 1, "residual").reshape(S, -1)
+
+    def qkv(self, valid, l):
+        qk = self.read(valid, "qkv", l, "qk").reshape(S, QD + DH)
+        vt = self.read(valid, "qkv", l, "vt").reshape(DH, -1)
+        q, k = qk[:, :QD], qk[:, QD:]
+        v = vt[:, _vt_column(np.arange(S))].T
+        return q, k, v
+
+    def prefix(self, l):
+        kv = self.inputs["prefix_kv"][l, :, 0, :, 0, :].astype(np.float64)  # [2][L][dh]
+        return kv[0], kv[1]
+
+    def close(self):
+        self.ex.close()
+
+
+@pytest.fixture(scope="module")
+def st():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = Stages()
+    yield c
+    c.close()
+
+
+def test_suffix_embedding(st):
+    got = st.read(816, "embed", 0, "residual").reshape(S, -1)
+    ref = st.orc.embed_suffix(st.inputs["state"][0], st.x[0], st.t)
+    check_stage(got, ref, "suffix embedding")
+
+
+@pytest.mark.parametrize("layer", [0, 17])
+def test_norm_qkv_rope(st, layer):
+    valid = 700
+    h = st.residual_before(valid, layer)
+    q, k, v = st.qkv(valid, layer)
+    rq, rk, rv = st.orc.stage_qkv(layer, h, valid + np.arange(S, dtype=np.float64))
+    check_stage(q, rq, f"layer {layer} q (norm + projection + RoPE)")
+    check_stage(k, rk, f"layer {layer} k (norm + projection + RoPE)")
+    check_stage(v, rv, f"layer {layer} v (norm + projection)")
+
+
+@pytest.mark.parametrize("valid", [0, 816, 700])
+@pytest.mark.parametrize("layer", [0, 17])
+def test_attention(st, valid, layer):
+    q, k, v = st.qkv(valid, layer)
+    got = st.read(valid, "attention", layer, "attn_out").reshape(S, QD)
+    kp, vp = st.prefix(layer)
+    ref = st.orc.stage_attention(q, k, v, kp, vp, valid)
+    check_stage(got, ref, f"layer {layer} attention valid {valid}")
+
+
+@pytest.mark.parametrize("layer", [0, 9, 17])
+def test_o_proj_residual(st, layer):
+    valid = 700
+    h = st.residual_before(valid, layer)
+    o = st.read(valid, "attention", layer, "attn_out").reshape(S, QD)
+    got = st.read(valid, "o_proj", layer, "residual").reshape(S, -1)
+    ref = st.orc.stage_o_proj(layer, h, o)
+    # the increment over the residual is the projection itself (the residual
+    # dominates the sum and would hide its error)
+    check_stage(got - h, ref - h, f"layer {layer} o_proj (increment)")
+    check_stage(got, ref, f"layer {layer} o_proj + residual")
+
+
+@pytest.mark.parametrize("layer", [0, 9, 17])
+def test_gate_up_geglu(st, layer):
+    valid = 700
+    h = st.read(valid, "o_proj", layer, "residual").reshape(S, -1)
+    got = st.read(valid, "gate_up", layer, "geglu").reshape(S, -1)
+    check_stage(got, st.orc.stage_gate_up(layer, h), f"layer {layer} norm + gate/up + GeGLU")
+
+
+@pytest.mark.parametrize("layer", [0, 9, 17])
+def test_down_residual(st, layer):
+    valid = 700
+    h = st.read(valid, "o_proj", layer, "residual").reshape(S, -1)
+    g = st.read(valid, "gate_up", layer, "geglu").reshape(S, -1)
+    got = st.read(valid, "down", layer, "residual").reshape(S, -1)
+    ref = st.orc.stage_down(layer, h, g)
+    check_stage(got - h, ref - h, f"layer {layer} down (increment)")
+    check_stage(got, ref, f"layer {layer} down + residual")
+
+
+def test_head_and_euler_update(st):
+    # the velocity from the last layer's residual, then one Euler step from
+    # t = 1 (pi0x_denoise with N = 1: x <- x - v)
+    valid = 700
+    d = st.dev
+    last = W1.shape.depth - 1
+    h = st.read(valid, "down", last, "residual").reshape(S, -1)
+    v = st.ex.denoise_step(d["prefix_kv"], st.valid_dev(valid), d["state"], st.x_dev, st.t)
+    torch.cuda.synchronize()
+    check_stage(v.cpu().numpy()[0], st.orc.stage_head(h), "final norm + action_out_proj (velocity)")
+    # Euler: the same stages at t = 1 on the noise
+    noise = d["noise"]
+    _say("debug read at t=1 for the Euler step")
+    h1 = st.ex.debug_until(d["prefix_kv"], st.valid_dev(valid), d["state"], noise, 1.0, "down", last, "residual")
+    x1 = st.ex.denoise(d["prefix_kv"], st.valid_dev(valid), d["state"], noise, 1)
+    torch.cuda.synchronize()
+    h1 = h1.cpu().numpy().astype(np.float64).reshape(S, -1)
+    ref = st.inputs["noise"][0].astype(np.float64) - st.orc.stage_head(h1)
+    check_stage(x1.cpu().numpy()[0], ref, "final norm + action_out_proj + Euler (N=1)")

@@ -34,6 +34,8 @@ def check_close(gpu, ref, dtype, what=""):
     _say(f"{what}: max|diff| {err:.3e} rel-L2 {rel:.3e}")
     if dtype == "fp32":
         assert err <= 1e-4, f"{what}: max|diff| {err}"
+    elif dtype == "bf16-head":  # a bare bf16 head output (no noise term): twice the loop's bar
+        assert err <= 6e-2 and rel <= 2e-2, f"{what}: max|diff| {err} rel-L2 {rel}"
     else:
         assert err <= 3e-2 and rel <= 1e-2, f"{what}: max|diff| {err} rel-L2 {rel}"
 
@@ -214,6 +216,25 @@ def test_full_bf16_b1_variants():
     try:
         check_close(c.run(3, "zero_to_one", False, True, True), c.ref(3, "zero_to_one", False, True, True), "bf16",
                     "pi0 bf16 B=1 zero_to_one+causal+blend N=3")
+    finally:
+        c.close()
+
+
+def test_full_bf16_b1_x_prediction():
+    # bf16 x-prediction at the full expert shape: on the 0 -> 1 grid the
+    # returned chunk is the dt-weighted mean of the head outputs, with no
+    # noise term, so it carries the relative error of one bf16 head
+    # evaluation.  That error is the sum of the per-stage roundings over 18
+    # layers (each stage a few 1e-3 in tests/test_gpu_stages.py); a float32
+    # emulation of the bf16 rounding points puts one head output at rel-L2
+    # 1.4e-2 - 1.6e-2 against the fp64 oracle.  The chunk is therefore held
+    # to the single-velocity bar: max|diff| <= 6e-2 and rel-L2 <= 2e-2.
+    w = synth.WORKLOADS["pi0_bf16_b1"].replace(name="pi0_bf16_b1_xpred", seed=43)
+    c = Case(w, norm_std=0.0)
+    try:
+        for causal, blend in [(False, False), (True, True)]:
+            check_close(c.run(3, "zero_to_one", True, causal, blend), c.ref(3, "zero_to_one", True, causal, blend),
+                        "bf16-head", f"pi0 bf16 B=1 zero_to_one+xpred causal={causal} blend={blend} N=3")
     finally:
         c.close()
 

@@ -470,3 +470,43 @@ def test_norm_touches_only_the_leading_features_and_none_is_identity():
             assert np.array_equal(y[:, 2:], x[:, 2:])
             assert not np.allclose(y[:, :2], x[:, :2])
     assert np.array_equal(oracle.apply_norm(x, None, False), x)
+
+
+# ----------------------------------------------------------------------------
+# Single stages (the per-kernel tests' references): chained, they are the
+# oracle's whole layer and velocity (page 1, _compute_layer_suffix_only and
+# denoise_step), computed by the C code the pins above check
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_stages_chain_to_the_layer(causal):
+    blob = synth.make_weights(TINY, seed=21, dtype="fp32", norm_std=0.1)
+    o = oracle.Oracle(TINY, blob)
+    rng = np.random.default_rng(4)
+    S, L, valid = TINY.suffix_len, 40, 33
+    h = rng.standard_normal((S, TINY.width))
+    kp, vp = rng.standard_normal((2, L, TINY.head_dim))
+    pos = valid + np.arange(S, dtype=np.float64)
+    for l in range(TINY.depth):
+        lw = o.layer_weights(l)
+        assert np.array_equal(lw["wq"], synth.view(blob, TINY, f"layers.{l}.q_proj"))
+        assert np.array_equal(lw["wdown"], synth.view(blob, TINY, f"layers.{l}.down_proj"))
+        q, k, v = o.stage_qkv(l, h, pos)
+        att = o.stage_attention(q, k, v, kp, vp, valid, causal)
+        h1 = o.stage_o_proj(l, h, att)
+        g = o.stage_gate_up(l, h1)
+        h2 = o.stage_down(l, h1, g)
+        ref = o.layer(l, h, kp, vp, valid, pos, causal)
+        assert np.allclose(h2, ref, rtol=1e-12, atol=1e-12)
+        h = ref
+
+
+def test_stage_head_is_the_velocity():
+    blob = synth.make_weights(TINY, seed=22, dtype="fp32", norm_std=0.1)
+    o = oracle.Oracle(TINY, blob)
+    rng = np.random.default_rng(5)
+    L, valid = 24, 20
+    state = rng.standard_normal(TINY.state_dim)
+    x = rng.standard_normal((TINY.horizon, TINY.action_dim))
+    kv = rng.standard_normal((TINY.depth, 2, L, TINY.num_kv_heads, TINY.head_dim))
+    h = o.expert_forward(o.embed_suffix(state, x, 0.4), kv, L, valid)
+    assert np.allclose(o.stage_head(h), o.velocity(state, x, 0.4, kv, L, valid), rtol=1e-12, atol=1e-12)

@@ -118,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.pi0x_prefix_set_timing.restype = i32
         L.pi0x_prefix_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.pi0x_prefix_read_timing.restype = i32
+        L.pi0x_debug_velocity_until.argtypes = [vp, i32, i32, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, vp, sz,
+                                                 vp]
+        L.pi0x_debug_velocity_until.restype = i32
         L.pi0x_expert_check_guards.argtypes = [vp, ctypes.POINTER(i32)]
         L.pi0x_expert_check_guards.restype = i32
         L.pi0x_prefix_check_guards.argtypes = [vp, ctypes.POINTER(i32)]
@@ -243,6 +246,16 @@ def pi0x_read_timing(h) -> tuple[int, dict]:
     cnt = (ctypes.c_int64 * n)()
     st = lib().pi0x_read_timing(h, ms, cnt)
     return st, {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+
+DEBUG_STAGES = {"embed": 0, "qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
+DEBUG_BUFFERS = {"residual": 0, "qk": 1, "vt": 2, "attn_out": 3, "geglu": 4}
+
+
+def pi0x_debug_velocity_until(h, batch, prefix_len, prefix_kv, valid, state, x_t, t, stage, layer, buffer, dst,
+                              dst_bytes, stream) -> int:
+    return lib().pi0x_debug_velocity_until(h, batch, prefix_len, prefix_kv, valid, state, x_t, float(t), stage, layer,
+                                           buffer, dst, dst_bytes, stream)
 
 
 def pi0x_expert_check_guards(h) -> tuple[int, int]:
@@ -398,6 +411,26 @@ class Expert:
         check(pi0x_denoise_step(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
                                 self._ptr(x_t), float(t), self._ptr(out), self._stream(stream)))
         return out
+
+    def debug_until(self, prefix_kv, valid_len, state, x_t, t: float, stage: str, layer: int, buffer: str,
+                    stream=None):
+        """pi0x_debug_velocity_until: one working buffer after `stage` of
+        `layer` of a single velocity evaluation, as a new device tensor
+        (float32 for "residual", the model dtype otherwise, flat)."""
+        import torch
+        c = self.cfg
+        B, L = self._validate(prefix_kv, valid_len, state, x_t, x_t, alias_ok=x_t)
+        R, S = B * (c.action_horizon + 1), c.action_horizon + 1
+        Sp = (S + 63) // 64 * 64
+        qd = c.num_heads * c.head_dim
+        n = {"residual": R * c.width, "qk": R * (qd + c.head_dim), "vt": B * c.head_dim * Sp,
+             "attn_out": R * qd, "geglu": R * c.mlp_dim}[buffer]
+        dt = torch.float32 if buffer == "residual" else model_dtype(c)
+        dst = torch.empty(n, dtype=dt, device=self.device)
+        check(pi0x_debug_velocity_until(self.h, B, L, self._ptr(prefix_kv), self._ptr(valid_len), self._ptr(state),
+                                        self._ptr(x_t), t, DEBUG_STAGES[stage], int(layer), DEBUG_BUFFERS[buffer],
+                                        dst.data_ptr(), dst.numel() * dst.element_size(), self._stream(stream)))
+        return dst
 
     def guard_violations(self) -> int:
         """Buffers of the handle that a kernel wrote past (0 is correct)."""

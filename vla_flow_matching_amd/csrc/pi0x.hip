@@ -99,7 +99,13 @@ struct Layer {
 // sampler of page 1.
 struct LoopOpts {
   int zero_to_one = 0, xpred = 0, causal = 0, blend = 0;
+  // pi0x_debug_velocity_until: stop after this stage (PI0X_DEBUG_AFTER_*) of
+  // this layer; -1 runs everything (the debug calls never use graphs)
+  int stop_stage = -1, stop_layer = -1;
   int bits() const { return zero_to_one | xpred << 1 | causal << 2 | blend << 3; }
+  bool stop_at(int stage, int layer) const {
+    return stop_stage == stage && (stage == PI0X_DEBUG_AFTER_EMBED || stop_layer == layer);
+  }
 };
 
 struct Key {
@@ -652,6 +658,7 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
     PI0X_TIMED(PI0X_KERNEL_SUFFIX_EMBED,
                (launch_gemm<T>(h, s, h->u, W, h->w_mo, AR, W, W,
                                EpiSuffixRows<T>{h->hbuf, hb, W, H, S, h->b_mo, h->ssq, np}, NormIn(), R)));
+    if (lo.stop_at(PI0X_DEBUG_AFTER_EMBED, 0)) return PI0X_OK;
     for (int l = 0; l < h->D; ++l) {
       const Layer& ly = h->layers[l];
       PI0X_TIMED(PI0X_KERNEL_QKV_ROPE,
@@ -659,12 +666,17 @@ pi0x_status enqueue(pi0x_expert* h, hipStream_t s, int B, int L, int N, const Lo
                                  EpiQkvRope<T>{(T*)h->qk, h->qd + h->dh, h->qd + h->dh, h->dh, S, h->rope_cs,
                                                (T*)h->vts, h->Sp},
                                  l == 0 ? nin : nin_down)));
+      if (lo.stop_at(PI0X_DEBUG_AFTER_QKV, l)) return PI0X_OK;
       PI0X_TIMED(PI0X_KERNEL_ATTENTION, launch_attn<T>(h, s, B, L, l, lo.causal));
+      if (lo.stop_at(PI0X_DEBUG_AFTER_ATTENTION, l)) return PI0X_OK;
       PI0X_TIMED(PI0X_KERNEL_O_PROJ, (launch_gemm<T>(h, s, h->o, h->qd, ly.wo, R, W, h->qd,
                                                      EpiResidual<T>{h->hbuf, hb, W, h->ssq, np})));
+      if (lo.stop_at(PI0X_DEBUG_AFTER_O_PROJ, l)) return PI0X_OK;
       PI0X_TIMED(PI0X_KERNEL_GATE_UP,
                  (launch_gemm<T>(h, s, hA, W, ly.wgu, R, 2 * h->M, W, EpiGeglu<T>{(T*)h->gbuf, h->M}, nin)));
+      if (lo.stop_at(PI0X_DEBUG_AFTER_GATE_UP, l)) return PI0X_OK;
       PI0X_TIMED(PI0X_KERNEL_DOWN, down_proj(ly));
+      if (lo.stop_at(PI0X_DEBUG_AFTER_DOWN, l)) return PI0X_OK;
     }
     const int last = (k == steps - 1);
     const EpiEuler epi{h->x, h->desc, h->b_out, H, S, h->A, first, last, N > 0 ? 0 : 1,
@@ -1296,6 +1308,45 @@ pi0x_status pi0x_denoise_step(pi0x_expert* h, int32_t batch, int32_t prefix_len,
                      v_out, t, nullptr, nullptr);
   PI0X_HIP(hipGetLastError());
   return run(h, batch, prefix_len, 0, LoopOpts{}, stream);
+}
+
+pi0x_status pi0x_debug_velocity_until(pi0x_expert* h, int32_t batch, int32_t prefix_len, const void* prefix_kv,
+                                      const int32_t* prefix_valid_len, const float* state, const float* x_t, float t,
+                                      int32_t stage, int32_t layer, int32_t buffer, void* dst, size_t dst_bytes,
+                                      hipStream_t stream) {
+  float* const no_out = reinterpret_cast<float*>(dst);  // never written: every stop comes before the head
+  PI0X_TRY(check_call(h, batch, prefix_len, prefix_kv, prefix_valid_len, state, x_t, no_out));
+  if (stage < PI0X_DEBUG_AFTER_EMBED || stage > PI0X_DEBUG_AFTER_DOWN)
+    return fail(PI0X_ERR_INVALID_ARG, "unknown debug stage");
+  if (stage != PI0X_DEBUG_AFTER_EMBED && (layer < 0 || layer >= h->D))
+    return fail(PI0X_ERR_INVALID_ARG, "layer out of range");
+  const size_t R = (size_t)batch * h->S, e = h->esz;
+  const void* src = nullptr;
+  size_t bytes = 0;
+  switch (buffer) {
+    case PI0X_DEBUG_RESIDUAL: src = h->hbuf; bytes = R * h->W * 4; break;
+    case PI0X_DEBUG_QK: src = h->qk; bytes = R * (h->qd + h->dh) * e; break;
+    case PI0X_DEBUG_VT: src = h->vts; bytes = (size_t)batch * h->dh * h->Sp * e; break;
+    case PI0X_DEBUG_ATTN_OUT: src = h->o; bytes = R * h->qd * e; break;
+    case PI0X_DEBUG_GEGLU: src = h->gbuf; bytes = R * h->M * e; break;
+    default: return fail(PI0X_ERR_INVALID_ARG, "unknown debug buffer");
+  }
+  if (!dst) return fail(PI0X_ERR_INVALID_ARG, "dst is NULL");
+  if (dst_bytes < bytes) return fail(PI0X_ERR_CAPACITY, "dst needs " + std::to_string(bytes) + " bytes");
+  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, stream, h->desc, prefix_kv, prefix_valid_len, state, x_t,
+                     nullptr, t, nullptr, nullptr);
+  PI0X_HIP(hipGetLastError());
+  LoopOpts lo;
+  lo.stop_stage = stage;
+  lo.stop_layer = layer;
+  const bool timing = h->timing;
+  h->timing = false;
+  const pi0x_status st = h->bf16() ? enqueue<bf16>(h, stream, batch, prefix_len, 0, lo)
+                                   : enqueue<float>(h, stream, batch, prefix_len, 0, lo);
+  h->timing = timing;
+  PI0X_TRY(st);
+  PI0X_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream));
+  return PI0X_OK;
 }
 
 pi0x_status pi0x_set_normalization(pi0x_expert* h, const pi0x_norm* state, const pi0x_norm* action) {
