@@ -1,24 +1,24 @@
-"""A second, independent fp64 formulation of the pi0 expert denoise loop, used
-only to cross-check the C oracle on small shapes.
+"""A second, independent fp64 formulation of the pi0 expert denoise loop and
+of the prefix pass, used only to cross-check the C oracle on small shapes.
 
-It differs from the oracle in every place a slip could hide:
-- whole-tensor torch ops instead of per-row loops;
-- the Hugging Face Gemma modules that page 1
-  ("vllm_omni/diffusion/models/pi0/modeling_pi0.py") itself calls for the
-  q/k/v/o projections, the gate/up/down MLP with the tanh GELU and
-  apply_rotary_pos_emb, all in float64;
-- masking as an additive bias of the page's mask constant (-2.3819763e38)
-  built from the cumulative-sum visibility rule of make_att_2d_masks, rather
-  than skipping keys;
-- grouped-query attention by explicitly repeating the kv head to every query
-  head instead of indexing the shared head.
+It is whole-tensor torch math written from the method's definition (page 1,
+"vllm_omni/diffusion/models/pi0/modeling_pi0.py": the suffix embedding, the
+block-causal suffix mask, the Gemma decoder layer with its (1 + w) RMSNorm,
+rotary embedding, grouped-query attention over cache + suffix, tanh-GELU
+GeGLU MLP, the final norm and action_out_proj; page 3 for the Wall-X loop
+variants), and it differs from the oracle's per-row C loops in every place a
+slip could hide:
+- the q, k and v projections are one einsum over the stacked weight matrices;
+- the rotary embedding multiplies complex numbers: feature j and feature
+  j + d/2 of a head are the real and imaginary part of one number, rotated by
+  exp(i * pos * base^(-2j/d));
+- attention weights are exp(score - logsumexp(visible scores)), visibility a
+  boolean tensor from the cumulative-sum rule (the oracle skips keys one by
+  one), and the kv heads are shared by index arithmetic inside the einsum;
+- the Gemma norm, SiLU and the tanh GELU are written out as tensor formulas.
 
-Hugging Face's GemmaRMSNorm and rotary module evaluate internally in float32,
-so for a float64 comparison this formulation writes the Gemma norm
-(h / sqrt(mean(h^2) + eps) * (1 + w)) as one whole-tensor float64 expression
-and computes the rotary angles in float64 from HF's inverse-frequency
-definition (base^(-2j/d)); tests pin both against the HF modules to float32
-accuracy.
+The Hugging Face Gemma modules are not used here; tests/test_oracle_pins.py
+pins the oracle's primitives against them separately.
 """
 from __future__ import annotations
 
@@ -26,41 +26,14 @@ import math
 
 import numpy as np
 import torch
-import torch.nn.functional as F
-from transformers import GemmaConfig
-from transformers.models.gemma.modeling_gemma import GemmaForCausalLM, apply_rotary_pos_emb
 
 from vla_flow_matching_amd import synth
 
-MASK_VALUE = -2.3819763e38
-
-
-def build_expert(shape: synth.ExpertShape, blob: np.ndarray, layout=synth.blob_layout) -> GemmaForCausalLM:
-    cfg = GemmaConfig(head_dim=shape.head_dim, hidden_size=shape.width, intermediate_size=shape.mlp_dim,
-                      num_attention_heads=shape.num_heads, num_hidden_layers=shape.depth,
-                      num_key_value_heads=shape.num_kv_heads, vocab_size=16, rms_norm_eps=shape.rms_eps,
-                      hidden_activation="gelu_pytorch_tanh", hidden_act="gelu_pytorch_tanh",
-                      rope_parameters={"rope_theta": shape.rope_theta, "rope_type": "default"})
-    m = GemmaForCausalLM(cfg).double().eval()
-    t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name, layout), dtype=np.float64))
-    with torch.no_grad():
-        for l, layer in enumerate(m.model.layers):
-            layer.input_layernorm.weight.copy_(t(f"layers.{l}.input_norm"))
-            layer.self_attn.q_proj.weight.copy_(t(f"layers.{l}.q_proj"))
-            layer.self_attn.k_proj.weight.copy_(t(f"layers.{l}.k_proj"))
-            layer.self_attn.v_proj.weight.copy_(t(f"layers.{l}.v_proj"))
-            layer.self_attn.o_proj.weight.copy_(t(f"layers.{l}.o_proj"))
-            layer.post_attention_layernorm.weight.copy_(t(f"layers.{l}.post_norm"))
-            layer.mlp.gate_proj.weight.copy_(t(f"layers.{l}.gate_proj"))
-            layer.mlp.up_proj.weight.copy_(t(f"layers.{l}.up_proj"))
-            layer.mlp.down_proj.weight.copy_(t(f"layers.{l}.down_proj"))
-        if layout is synth.blob_layout:
-            m.model.norm.weight.copy_(t("final_norm"))
-    return m
-
 
 def rope_tables_f64(positions: torch.Tensor, head_dim: int, base: float):
-    """cos/sin [B, S, head_dim] for integer positions, angles in float64."""
+    """cos/sin [..., head_dim] of the rotate-half convention for integer
+    positions, angles in float64 (inverse frequencies base^(-2j/d), repeated
+    for the two halves)."""
     inv_freq = 1.0 / (base ** (torch.arange(0, head_dim, 2, dtype=torch.float64) / head_dim))
     ang = positions.to(torch.float64)[..., None] * inv_freq
     ang = torch.cat([ang, ang], dim=-1)
@@ -68,29 +41,96 @@ def rope_tables_f64(positions: torch.Tensor, head_dim: int, base: float):
 
 
 def gemma_norm(h: torch.Tensor, w: torch.Tensor, eps: float) -> torch.Tensor:
-    return h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + eps) * (1.0 + w)
+    return h / torch.sqrt((h * h).mean(-1, keepdim=True) + eps) * (1.0 + w)
+
+
+def gelu_tanh(x: torch.Tensor) -> torch.Tensor:
+    return 0.5 * x * (1.0 + torch.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def silu(x: torch.Tensor) -> torch.Tensor:
+    return x / (1.0 + torch.exp(-x))
+
+
+def rotate(u: torch.Tensor, pos: torch.Tensor, base: float) -> torch.Tensor:
+    """u [B, S, heads, d] at positions pos [B, S]: the pair (u_j, u_{j+d/2}) as
+    the complex number u_j + i u_{j+d/2}, multiplied by exp(i pos theta_j)."""
+    d = u.shape[-1]
+    theta = base ** (-torch.arange(0, d // 2, dtype=torch.float64) * 2.0 / d)
+    rot = torch.polar(torch.ones_like(theta), pos.to(torch.float64)[..., None] * theta)  # [B, S, d/2]
+    z = torch.complex(u[..., : d // 2], u[..., d // 2:]) * rot[:, :, None, :]
+    return torch.cat([z.real, z.imag], dim=-1)
 
 
 def time_features(t: torch.Tensor, dim: int, min_p: float, max_p: float) -> torch.Tensor:
-    """[B, dim] sine/cosine features; log-spaced periods between min_p and max_p."""
+    """[B, dim]: sines then cosines of t * 2 pi / period, periods log-spaced
+    from min_p to max_p."""
     frac = torch.linspace(0.0, 1.0, dim // 2, dtype=torch.float64)
     omega = (2 * math.pi) / (min_p * (max_p / min_p) ** frac)
     arg = t.to(torch.float64)[:, None] * omega[None, :]
     return torch.cat([arg.sin(), arg.cos()], dim=1)
 
 
+class _Layers:
+    """A decoder stack's weights as float64 tensors, the projections stacked."""
+
+    def __init__(self, shape: synth.ExpertShape, blob: np.ndarray, layout):
+        t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name, layout), dtype=np.float64))
+        self.layers = []
+        for l in range(shape.depth):
+            self.layers.append({
+                "in_norm": t(f"layers.{l}.input_norm"),
+                "wqkv": torch.cat([t(f"layers.{l}.q_proj"), t(f"layers.{l}.k_proj"), t(f"layers.{l}.v_proj")]),
+                "wo": t(f"layers.{l}.o_proj"),
+                "post_norm": t(f"layers.{l}.post_norm"),
+                "wgu": torch.stack([t(f"layers.{l}.gate_proj"), t(f"layers.{l}.up_proj")]),
+                "wd": t(f"layers.{l}.down_proj"),
+            })
+
+
+def _layer(s, w, h, pos, keys, vals, visible):
+    """One decoder layer over query rows h [B, S, W].  keys / vals: the cached
+    keys and values in front of this layer's own [B, Lc, n_kv, d] (Lc may be 0);
+    visible [B, S, Lc + S].  Returns (h_out, k_own, v_own) with k_own after RoPE."""
+    nh, nkv, d = s.num_heads, s.num_kv_heads, s.head_dim
+    B, S, _ = h.shape
+    y = gemma_norm(h, w["in_norm"], s.rms_eps)
+    qkv = torch.einsum("bsw,ow->bso", y, w["wqkv"])
+    q = qkv[..., : nh * d].reshape(B, S, nh, d)
+    k = qkv[..., nh * d:(nh + nkv) * d].reshape(B, S, nkv, d)
+    v = qkv[..., (nh + nkv) * d:].reshape(B, S, nkv, d)
+    q, k = rotate(q, pos, s.rope_theta), rotate(k, pos, s.rope_theta)
+    K = torch.cat([keys, k], dim=1)
+    V = torch.cat([vals, v], dim=1)
+    # query head n reads kv head n // (nh / nkv): split the query heads as (kv head, group member)
+    qg = q.reshape(B, S, nkv, nh // nkv, d)
+    score = torch.einsum("bsgrd,bkgd->bgrsk", qg, K) / math.sqrt(d)
+    vis = visible[:, None, None]
+    score = torch.where(vis, score, torch.tensor(-math.inf, dtype=torch.float64))
+    lse = torch.logsumexp(score, dim=-1, keepdim=True)
+    any_vis = vis.any(-1, keepdim=True)
+    p = torch.where(vis & any_vis, torch.exp(score - torch.where(any_vis, lse, torch.zeros_like(lse))), 0.0)
+    o = torch.einsum("bgrsk,bkgd->bsgrd", p, V).reshape(B, S, nh * d)
+    h = h + torch.einsum("bsi,oi->bso", o, w["wo"])
+    y = gemma_norm(h, w["post_norm"], s.rms_eps)
+    gu = torch.einsum("bsw,cmw->cbsm", y, w["wgu"])
+    h = h + torch.einsum("bsm,om->bso", gelu_tanh(gu[0]) * gu[1], w["wd"])
+    return h, k, v
+
+
 class PageFormulation:
     def __init__(self, shape: synth.ExpertShape, blob: np.ndarray):
         self.s = shape
-        self.expert = build_expert(shape, blob)
+        self.stack = _Layers(shape, blob, synth.blob_layout)
         t = lambda name: torch.from_numpy(np.array(synth.view(blob, shape, name), dtype=np.float64))
+        self.final_norm = t("final_norm")
         self.lin = {}
         for nm in ("state_proj", "action_in_proj", "action_time_mlp_in", "action_time_mlp_out", "action_out_proj"):
             self.lin[nm] = (t(nm + ".weight"), t(nm + ".bias"))
 
     def _linear(self, name, x):
         w, b = self.lin[name]
-        return F.linear(x, w, b)
+        return torch.einsum("...i,oi->...o", x, w) + b
 
     def suffix_embedding(self, state, x, t):
         s = self.s
@@ -98,14 +138,14 @@ class PageFormulation:
         tfeat = time_features(t, s.width, s.min_period, s.max_period)
         act = self._linear("action_in_proj", x)
         fused = torch.cat([act, tfeat[:, None, :].expand(-1, act.shape[1], -1)], dim=-1)
-        fused = self._linear("action_time_mlp_out", F.silu(self._linear("action_time_mlp_in", fused)))
+        fused = self._linear("action_time_mlp_out", silu(self._linear("action_time_mlp_in", fused)))
         return torch.cat([state_tok, fused], dim=1)
 
     def visibility(self, valid: torch.Tensor, L: int, causal: bool = False) -> torch.Tensor:
         """bool [B, S, L + S]: prefix key j visible iff j < valid; suffix key c visible
         to query r iff cumsum(ar)[c] <= cumsum(ar)[r] with ar = [1, 1, 0, ..., 0].
-        causal: the suffix block is overwritten by a lower triangle, as page 3
-        (Wall-X, generate_flow_action) does under causal_action_attention_mask."""
+        causal: the suffix block is a lower triangle instead, as page 3
+        (Wall-X, generate_flow_action) sets it under causal_action_attention_mask."""
         S = self.s.suffix_len
         B = valid.shape[0]
         pre = (torch.arange(L)[None, :] < valid[:, None])[:, None, :].expand(B, S, L)
@@ -120,35 +160,19 @@ class PageFormulation:
     def velocity(self, state, x, t, kv, valid, causal: bool = False):
         """state [B, Sd], x [B, H, A], t [B], kv [depth, 2, B, L, n_kv, dh], valid [B] -> v [B, H, A]."""
         s = self.s
-        B, L = kv.shape[2], kv.shape[3]
+        L = kv.shape[3]
         h = self.suffix_embedding(state, x, t)
-        bias = torch.where(self.visibility(valid, L, causal), 0.0, MASK_VALUE).to(torch.float64)[:, None]
+        vis = self.visibility(valid, L, causal)
         pos = valid[:, None].to(torch.int64) + torch.arange(s.suffix_len)[None, :]
-        cos, sin = rope_tables_f64(pos, s.head_dim, s.rope_theta)
-        rep = s.num_heads // s.num_kv_heads
-        for l, layer in enumerate(self.expert.model.layers):
-            att = layer.self_attn
-            y = gemma_norm(h, layer.input_layernorm.weight, s.rms_eps)
-            q = att.q_proj(y).view(B, -1, s.num_heads, s.head_dim).transpose(1, 2)
-            k = att.k_proj(y).view(B, -1, s.num_kv_heads, s.head_dim).transpose(1, 2)
-            v = att.v_proj(y).view(B, -1, s.num_kv_heads, s.head_dim).transpose(1, 2)
-            q, k = apply_rotary_pos_emb(q, k, cos, sin, unsqueeze_dim=1)
-            kp = kv[l, 0].permute(0, 2, 1, 3)   # [B, n_kv, L, dh]
-            vp = kv[l, 1].permute(0, 2, 1, 3)
-            k = torch.cat([kp, k], dim=2).repeat_interleave(rep, dim=1)
-            v = torch.cat([vp, v], dim=2).repeat_interleave(rep, dim=1)
-            scores = q @ k.transpose(-1, -2) / math.sqrt(s.head_dim) + bias
-            o = torch.softmax(scores, dim=-1) @ v
-            o = o.transpose(1, 2).reshape(B, s.suffix_len, s.num_heads * s.head_dim)
-            h = h + att.o_proj(o)
-            h = h + layer.mlp(gemma_norm(h, layer.post_attention_layernorm.weight, s.rms_eps))
-        h = gemma_norm(h, self.expert.model.norm.weight, s.rms_eps)
+        for l, w in enumerate(self.stack.layers):
+            h, _, _ = _layer(s, w, h, pos, kv[l, 0], kv[l, 1], vis)
+        h = gemma_norm(h, self.final_norm, s.rms_eps)
         return self._linear("action_out_proj", h[:, 1:])
 
     def denoise(self, inputs: dict, num_steps: int) -> np.ndarray:
         f = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
         kv, valid = f(inputs["prefix_kv"]), torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
-        kv = torch.nan_to_num(kv, nan=0.0)  # additive masking multiplies padding by 0; keep it finite
+        kv = torch.nan_to_num(kv, nan=0.0)  # padded keys are never visible; keep their values finite
         state, x = f(inputs["state"]), f(inputs["noise"])
         B = state.shape[0]
         with torch.no_grad():
@@ -161,43 +185,39 @@ class PageFormulation:
     def denoise_wallx(self, inputs: dict, num_steps: int, x_pred: bool = False, causal: bool = False,
                       dof_mask=None, padding=None) -> np.ndarray:
         """The loop of page 3 (Wall-X, generate_flow_action) on this expert: a float32
-        time grid linspace(0, 1, N + 1); a first (prefill) step at times[0] whose
-        velocity takes the padding blend; then Euler over times[1:] with the
-        cached prefix.  x_pred: the head's output minus the initial noise."""
+        time grid from 0 to 1 in num_steps steps; a first step at its first point
+        whose velocity takes the padding blend; then Euler over the rest.
+        x_pred: the head's output minus the initial noise."""
         f = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
         kv, valid = f(inputs["prefix_kv"]), torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
         kv = torch.nan_to_num(kv, nan=0.0)
         state, noise = f(inputs["state"]), f(inputs["noise"])
         B = state.shape[0]
-        times = torch.linspace(0.0, 1.0, num_steps + 1, dtype=torch.float64).to(torch.float32).to(torch.float64)
+        times = torch.tensor([float(np.float32(k / num_steps)) for k in range(num_steps + 1)], dtype=torch.float64)
 
-        def step(tk, x):
+        def velocity(tk, x):
             v = self.velocity(state, x, torch.full((B,), float(tk), dtype=torch.float64), kv, valid, causal)
             return v - noise if x_pred else v
 
         with torch.no_grad():
             x = noise.clone()
-            v0 = step(times[0], x)
-            if padding is not None:
-                m = f(dof_mask)
-                if not bool((m == 1).all()):
-                    v0 = (f(padding) - x) * (1 - m) + v0 * m
-            x = x + (times[1] - times[0]) * v0
-            for i in range(1, num_steps):
-                x = x + (times[i + 1] - times[i]) * step(times[i], x)
+            for i in range(num_steps):
+                v = velocity(times[i], x)
+                if i == 0 and padding is not None:
+                    m = f(dof_mask)
+                    v = (f(padding) - x) * (1 - m) + v * m
+                x = x + (times[i + 1] - times[i]) * v
         return x.numpy()
 
 
 class PrefixFormulation:
-    """The prefix pass of page 1 (sample_actions: embed_prefix's all-zero
-    autoregressive mask, make_att_2d_masks with the pad mask, positions
-    cumsum(pad) - 1; _compute_layer_prefix_only per layer) in whole-tensor
-    torch float64 with the Hugging Face Gemma modules, the additive mask bias
-    and an explicit repeat of the kv head."""
+    """The prefix pass of page 1 (all prefix tokens attend to each other's
+    valid tokens, positions 0..valid-1; per layer the post-RoPE keys and the
+    values go to the cache), in the same whole-tensor form."""
 
     def __init__(self, shape: synth.ExpertShape, blob: np.ndarray):
         self.s = shape
-        self.model = build_expert(shape, blob, layout=synth.layer_layout)
+        self.stack = _Layers(shape, blob, synth.layer_layout)
 
     def prefill(self, inputs: dict) -> np.ndarray:
         """cache [depth][2][B][L][n_kv][dh]: per layer the post-RoPE k and v."""
@@ -205,28 +225,14 @@ class PrefixFormulation:
         emb = torch.from_numpy(np.nan_to_num(np.array(inputs["embeddings"], dtype=np.float64), nan=0.0))
         valid = torch.from_numpy(np.array(inputs["valid_len"], dtype=np.int64))
         B, L, _ = emb.shape
-        pad = torch.arange(L)[None, :] < valid[:, None]
-        ar = torch.zeros((B, L), dtype=torch.int64)
-        cum = torch.cumsum(ar, dim=1)
-        att = (cum[:, None, :] <= cum[:, :, None]) & (pad[:, None, :] & pad[:, :, None])
-        bias = torch.where(att, 0.0, MASK_VALUE).to(torch.float64)[:, None]
-        pos = torch.cumsum(pad.to(torch.int64), dim=1) - 1
-        cos, sin = rope_tables_f64(pos, s.head_dim, s.rope_theta)
-        rep = s.num_heads // s.num_kv_heads
+        real = torch.arange(L)[None, :] < valid[:, None]
+        vis = real[:, None, :] & real[:, :, None]
+        pos = (torch.cumsum(real.to(torch.int64), dim=1) - 1).clamp(min=0)
+        empty = torch.zeros((B, 0, s.num_kv_heads, s.head_dim), dtype=torch.float64)
         h = emb
         cache = []
         with torch.no_grad():
-            for layer in self.model.model.layers:
-                att_m = layer.self_attn
-                y = gemma_norm(h, layer.input_layernorm.weight, s.rms_eps)
-                q = att_m.q_proj(y).view(B, L, s.num_heads, s.head_dim).transpose(1, 2)
-                k = att_m.k_proj(y).view(B, L, s.num_kv_heads, s.head_dim).transpose(1, 2)
-                v = att_m.v_proj(y).view(B, L, s.num_kv_heads, s.head_dim).transpose(1, 2)
-                q, k = apply_rotary_pos_emb(q, k, cos, sin, unsqueeze_dim=1)
-                cache.append(torch.stack([k.transpose(1, 2), v.transpose(1, 2)]))  # [2, B, L, n_kv, dh]
-                kr, vr = k.repeat_interleave(rep, dim=1), v.repeat_interleave(rep, dim=1)
-                scores = q @ kr.transpose(-1, -2) / math.sqrt(s.head_dim) + bias
-                o = (torch.softmax(scores, dim=-1) @ vr).transpose(1, 2).reshape(B, L, -1)
-                h = h + att_m.o_proj(o)
-                h = h + layer.mlp(gemma_norm(h, layer.post_attention_layernorm.weight, s.rms_eps))
+            for w in self.stack.layers:
+                h, k, v = _layer(s, w, h, pos, empty, empty, vis)
+                cache.append(torch.stack([k, v]))  # [2, B, L, n_kv, dh]
         return torch.stack(cache).numpy()
