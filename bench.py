@@ -160,7 +160,8 @@ def csrc_digest() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vla_flow_matching_amd", "csrc")
-    for p in sorted(os.listdir(csrc)) + ["../../include/pi0x.h"]:
+    # the kernels' sources and the header (not the C++ driver that only calls the ABI)
+    for p in sorted(f for f in os.listdir(csrc) if f != "denoise_driver.cpp") + ["../../include/pi0x.h"]:
         with open(os.path.join(csrc, p), "rb") as f:
             h.update(p.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -180,6 +181,32 @@ def measured_traffic(workload: str, kernel: str):
     if not e or e.get("csrc_sha256") != csrc_digest():
         return None
     return float(e["bytes_per_launch"])
+
+
+def _profile_entry(filename: str, workload: str):
+    """A workload's entry of a committed counter summary in profiles/, or None
+    when absent or taken on different kernel code."""
+    try:
+        with open(os.path.join(ROOT, "profiles", filename)) as f:
+            e = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not e or e.get("csrc_sha256") != csrc_digest():
+        return None
+    return e
+
+
+def measured_mfma_busy(workload: str, kernel: str):
+    """Share of the kernel's SIMD-cycles with the matrix pipe busy, from the
+    committed SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES pass, or None."""
+    e = _profile_entry("mfma_busy.json", workload)
+    return None if e is None else e.get("mfma_busy", {}).get(kernel)
+
+
+def measured_call_bytes(workload: str):
+    """HBM bytes of one call (all kernels, scaled FETCH_SIZE + WRITE_SIZE), or None."""
+    e = _profile_entry("hbm_traffic.json", workload)
+    return None if e is None or "per_call_bytes" not in e else float(e["per_call_bytes"])
 
 
 def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2, latency_calls: int = 100):
@@ -252,6 +279,10 @@ def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2, late
         roof = {"bound": "mfma", "achieved": u["flops"] / avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(name, dom)
+    # counter-derived rates: the measured HBM bytes over the same launch time,
+    # and the matrix pipes' busy share from the MFMA counters
+    roof["traffic_GBps"] = roof["traffic"] / avg_s / 1e9 if roof["traffic"] else None
+    roof["mfma_busy"] = measured_mfma_busy(name, dom)
     roof["kernel"] = dom
     roof["per_launch"] = {"bytes": u["bytes"], "flops": u["flops"], "avg_us": kern[dom]["avg_us"]}
     sec = ms * 1e-3
@@ -259,6 +290,9 @@ def run_workload(name: str, steps: int, warmup: int, timing_calls: int = 2, late
              "achieved_TFLOPs": counts["flops"] / sec / 1e12,
              "mfma_frac": counts["flops"] / sec / 1e12 / (MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS),
              "bytes_per_call": counts["bytes"], "flops_per_call": counts["flops"]}
+    cb = measured_call_bytes(name)
+    whole["counter_bytes_per_call"] = cb
+    whole["counter_GBps"] = cb / sec / 1e9 if cb else None
     return {"workload": w, "ms": ms, "value": w.batch / sec, "roofline": roof, "kernels": kern, "whole_loop": whole,
             "latency": dist, "inputs": inputs}
 

@@ -4,12 +4,14 @@
 // uniform weights (standard deviation 0.02), puts the inputs in device memory
 // (prefix K/V, valid lengths = prefix_len, state and noise), and makes
 // `--calls` pi0x_denoise calls, each synchronized.  With
+// --eager the calls run their kernels directly (no captured graph), as the
+// library's kernel-timing mode does.  With
 // --copy-calibration-mib M it first copies M MiB device to device once, a
 // transfer of known size against which hardware byte counters are scaled.
 // It is what hardware-counter runs (rocprofv3 --pmc) execute: no Python, no
 // torch, one process that only does this.
 //
-//   denoise_driver [--batch B] [--prefix-len L] [--steps N] [--calls C] [--copy-calibration-mib M]
+//   denoise_driver [--batch B] [--prefix-len L] [--steps N] [--calls C] [--eager] [--copy-calibration-mib M]
 //
 // Exit status 0 on success; any failing call prints pi0x_last_error() and exits 1.
 #include <hip/hip_runtime.h>
@@ -65,6 +67,12 @@ int arg_int(int argc, char** argv, const char* name, int def) {
   return def;
 }
 
+bool arg_flag(int argc, char** argv, const char* name) {
+  for (int i = 1; i < argc; ++i)
+    if (std::strcmp(argv[i], name) == 0) return true;
+  return false;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -83,6 +91,7 @@ int main(int argc, char** argv) {
   cfg.max_batch = B;
   cfg.max_prefix_len = L > 0 ? L : 1;
   if (cfg.max_steps < N) cfg.max_steps = N;
+  if (arg_flag(argc, argv, "--eager")) cfg.use_graphs = 0;
   const size_t nw = pi0x_weight_count(&cfg);
   if (nw == 0) {
     std::fprintf(stderr, "pi0x_weight_count: invalid config\n");
