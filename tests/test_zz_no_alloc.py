@@ -142,3 +142,36 @@ def test_noalloc_rejects_float32_handles():
         assert e.value.status == binding.PI0X_ERR_DTYPE
     finally:
         ex.close()
+
+
+def test_noalloc_under_stream_capture(b1):
+    # the use it exists for: captured into the caller's own graph (every node
+    # a kernel: no memset or copy nodes), replayed several times with other
+    # eager work and synchronizations between the replays
+    ex, dev = b1
+    kv, v = _inputs(dev, 816, 750)
+    state, noise = dev["state"], dev["noise"]
+    eager = torch.empty_like(noise)
+    _say("pi0x_denoise_noalloc eager reference")
+    ex.denoise_noalloc(kv, v, state, noise, eager, 4)
+    torch.cuda.synchronize()
+    ref = eager.cpu().numpy()
+    out = torch.full_like(noise, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    _say("capture pi0x_denoise_noalloc")
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ex.denoise_noalloc(kv, v, state, noise, out, 4)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        _say(f"replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), f"replay {r} differs from the eager call"
+        # other work between replays, on the same handle and array
+        ex.denoise(kv, v, state, noise, 2)
+        torch.cuda.synchronize()
