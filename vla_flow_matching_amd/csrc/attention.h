@@ -60,7 +60,7 @@ struct AttnArgs {
   int causal;  // suffix mask: 0 pi0 block rule, 1 lower triangle
   int prefill;  // prefix pass: prefix keys only
   int splits, tiles;
-  float* partial;  // splits > 1, per (B, tile, split, QT-tile): float32 max and sum [2][threads],
+  float* partial;  // splits > 1, per (B, tile, split, QT-tile): float32 reference maximum (log2 units) and sum [2][threads],
                    // then the unnormalised outputs in the model dtype [head_dim/16][threads][4]
 };
 
@@ -102,9 +102,19 @@ constexpr size_t attn_smem_bytes() {
 // element offset of 16-byte chunk ch (of 8 bf16) of swizzled row r (64 elements)
 __device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r >> 1) & 7)) << 3); }
 
-// exp for the softmax: the hardware exp2 path in bf16 mode, libm expf in float32 mode.
-template <typename T> __device__ __forceinline__ float fexp(float x) { return expf(x); }
-template <> __device__ __forceinline__ float fexp<bf16>(float x) { return __expf(x); }
+// The softmax runs in base 2: scores are scaled by scale * log2(e) and the
+// probabilities are 2^x (the same numbers as e^(scale * s)).  bf16 mode uses
+// the hardware exp2 instruction, float32 mode libm's exp2f.
+template <typename T> __device__ __forceinline__ float fexp2(float x) { return exp2f(x); }
+template <> __device__ __forceinline__ float fexp2<bf16>(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+// The reference maximum of a query moves only when a score exceeds it by
+// more than this (log2 units), so most key blocks skip the rescale of the
+// output accumulators; in between, probabilities stay below 2^8 (exact in
+// float32, and in bf16 only their 8-bit mantissa is rounded, as before).
+constexpr float kRefSlack = 8.f;
+// Initial reference: finite, so that x - m never meets -inf - (-inf).
+constexpr float kRefInit = -3.0e38f;
 
 // Four consecutive split-partial outputs as one access: 16 bytes of float32
 // or 8 bytes of bf16 (the bf16 path keeps its unnormalised partial outputs in
@@ -240,11 +250,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < QT; ++t)
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max (same on the 4 lanes of a query) and this lane's share of the sum, per query tile
+  // reference maximum in log2 units (same on the 4 lanes of a query) and this
+  // lane's share of the sum, per query tile
+  const float c2 = a.scale * kLog2e;
   float m_run[QT], l_run[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    m_run[t] = -INFINITY;
+    m_run[t] = kRefInit;
     l_run[t] = 0.f;
   }
 
@@ -282,49 +294,69 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t][kt]);
       }
-    float sc[QT][KT][4];
-    // suffix blocks: the state token (query s = 0) sees only key 0; with
-    // causal, query s sees keys 0..s
+    // masks apply only to a block with a key past some query's limit: the
+    // partial last prefix block and the suffix blocks (where the state token,
+    // query s = 0, sees only key 0, and with causal query s sees keys 0..s)
+    float sc[QT][KT][4], lmax[QT];
+    if (!pre || base + KB > lim) {
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int tlim = pre ? lim : (a.causal || qs[t] == 0) ? min(lim, qs[t] + 1) : lim;
+      for (int t = 0; t < QT; ++t) {
+        const int tlim = pre ? lim : (a.causal || qs[t] == 0) ? min(lim, qs[t] + 1) : lim;
+        lmax[t] = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = base + kt * 16 + g * 4 + e;
-          sc[t][kt][e] = key < tlim ? acc[t][kt][e] * a.scale : -INFINITY;
-        }
+          for (int e = 0; e < 4; ++e) {
+            const int key = base + kt * 16 + g * 4 + e;
+            sc[t][kt][e] = key < tlim ? acc[t][kt][e] : -INFINITY;
+            lmax[t] = fmaxf(lmax[t], sc[t][kt][e]);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        lmax[t] = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[t][kt][e] = acc[t][kt][e];
+            lmax[t] = fmaxf(lmax[t], sc[t][kt][e]);
+          }
+      }
     }
-    float m_new[QT];
+    // the reference moves (with the rescale of sum and outputs by
+    // 2^(old - new)) only when some lane of the wave has a score more than
+    // kRefSlack above its query's reference; the new reference is the
+    // query's maximum so far, taken over its 4 lanes
+    bool move = false;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      float bmax = -INFINITY;
+    for (int t = 0; t < QT; ++t) move |= lmax[t] * c2 > m_run[t] + kRefSlack;
+    if (__any(move)) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+      for (int t = 0; t < QT; ++t) {
+        float r = fmaxf(lmax[t], __shfl_xor(lmax[t], 16, 64));
+        r = fmaxf(r, __shfl_xor(r, 32, 64));
+        const float mn = fmaxf(m_run[t], r * c2);
+        const float alpha = fexp2<T>(m_run[t] - mn);
+        l_run[t] *= alpha;
+        m_run[t] = mn;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sc[t][kt][e]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      m_new[t] = fmaxf(m_run[t], bmax);
-      const float alpha = (m_new[t] == -INFINITY) ? 1.f : fexp<T>(m_run[t] - m_new[t]);
-      l_run[t] *= alpha;
-      m_run[t] = m_new[t];
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        o[t][d][0] *= alpha; o[t][d][1] *= alpha; o[t][d][2] *= alpha; o[t][d][3] *= alpha;
+        for (int d = 0; d < ND; ++d) {
+          o[t][d][0] *= alpha; o[t][d][1] *= alpha; o[t][d][2] *= alpha; o[t][d][3] *= alpha;
+        }
       }
     }
 #pragma unroll
     for (int ks2 = 0; ks2 < KS; ++ks2) {
       // probabilities of keys 32*ks2 + (i/4)*16 + 4g + i%4 as the PV operand
+      // (a masked key: 2^-inf = 0)
       Frag<T> pf[QT];
 #pragma unroll
       for (int t = 0; t < QT; ++t)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float x = sc[t][2 * ks2 + i / 4][i % 4];
-          const float e = (x == -INFINITY) ? 0.f : fexp<T>(x - m_new[t]);
+          const float e = fexp2<T>(fmaf(sc[t][2 * ks2 + i / 4][i % 4], c2, -m_run[t]));
           l_run[t] += e;
           set_frag(pf[t], i, e);
         }
@@ -413,14 +445,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < ZC; ++k)
         if (z0 + k < a.splits) mb = fmaxf(mb, vm[k]);
-      const float s0 = (m == -INFINITY) ? 0.f : fexp<T>(m - mb);
+      const float s0 = (m == -INFINITY) ? 0.f : fexp2<T>(m - mb);
       l *= s0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] *= s0;
 #pragma unroll
       for (int k = 0; k < ZC; ++k) {
         if (z0 + k >= a.splits) continue;
-        const float w = (vm[k] == -INFINITY) ? 0.f : fexp<T>(vm[k] - mb);
+        const float w = (vm[k] == -INFINITY) ? 0.f : fexp2<T>(vm[k] - mb);
         l += w * vl[k];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] += w * vo[k][e];
