@@ -145,6 +145,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int LDK = AttnLds<T, DH>::LDK;
   constexpr int LDV = AttnLds<T, DH>::LDV;
   constexpr int NC = DH / 32, ND = DH / 16;
+  // fragments per read-ahead group: a feature chunk's KT key tiles for K, 4
+  // feature tiles for V^T; float32 fragments take twice the registers (the
+  // head_dim 256 kernel would spill), so that path reads one ahead
+  constexpr int KG = sizeof(T) == 2 ? KT : 1;
+  constexpr int VG = sizeof(T) != 2 ? 1 : ND % 4 == 0 ? 4 : ND % 2 == 0 ? 2 : 1;
   constexpr int NVEC = KB * DH / VE;        // 16-byte vectors of K (and of V^T) per key block
   constexpr int KVEC = (NVEC + NT - 1) / NT;  // per thread
   constexpr bool FULL = NVEC % NT == 0;
@@ -284,16 +289,32 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int t = 0; t < QT; ++t)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The fragments of read-ahead group gi+1 are read while group gi's
+    // MFMAs run, so several LDS reads are in flight behind every MFMA (the
+    // compiler otherwise sinks each read next to its MFMA, one in flight);
+    // the scheduling barriers keep that order.  Fragment j is feature chunk
+    // j / KT of key tile j % KT.
+    Frag<T> kf[2][KG];
+    auto kread = [&](int gi, Frag<T>* dst) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        Frag<T> kf;
-        const int row = kt * 16 + (lane & 15);
-        load8(kf, &ks[SWZ ? (c >> 1) * (KB * 64) + swz64(row, (c & 1) * 4 + g) : row * LDK + c * 32 + g * 8]);
-#pragma unroll
-        for (int t = 0; t < QT; ++t) mma32(kf, qf[t][c], acc[t][kt]);
+      for (int i = 0; i < KG; ++i) {
+        const int c = (gi * KG + i) / KT, row = (gi * KG + i) % KT * 16 + (lane & 15);
+        load8(dst[i], &ks[SWZ ? (c >> 1) * (KB * 64) + swz64(row, (c & 1) * 4 + g) : row * LDK + c * 32 + g * 8]);
       }
+    };
+    kread(0, kf[0]);
+#pragma unroll
+    for (int gi = 0; gi < NC * KT / KG; ++gi) {
+      if (gi + 1 < NC * KT / KG) kread(gi + 1, kf[(gi + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < KG; ++i) {
+        const int c = (gi * KG + i) / KT, kt = (gi * KG + i) % KT;
+#pragma unroll
+        for (int t = 0; t < QT; ++t) mma32(kf[gi & 1][i], qf[t][c], acc[t][kt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // masks apply only to a block with a key past some query's limit: the
     // partial last prefix block and the suffix blocks (where the state token,
     // query s = 0, sees only key 0, and with causal query s sees keys 0..s)
@@ -360,14 +381,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
           l_run[t] += e;
           set_frag(pf[t], i, e);
         }
+      // V^T fragments in read-ahead groups of VG feature tiles, as for K;
+      // keys 32 ks2 + {4g .. 4g+3, 16+4g .. 16+4g+3} are contiguous in the
+      // vt_pos order
+      Frag<T> vf[2][VG];
+      auto vread = [&](int dg, Frag<T>* dst) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        // keys 32 ks2 + {4g .. 4g+3, 16+4g .. 16+4g+3}: contiguous in the vt_pos order
-        Frag<T> vf;
-        const int row = d * 16 + (lane & 15);
-        load8(vf, &vt[SWZ ? swz64(row, ks2 * 4 + g) : row * LDV + ks2 * 32 + g * 8]);
+        for (int j = 0; j < VG; ++j) {
+          const int row = (dg * VG + j) * 16 + (lane & 15);
+          load8(dst[j], &vt[SWZ ? swz64(row, ks2 * 4 + g) : row * LDV + ks2 * 32 + g * 8]);
+        }
+      };
+      vread(0, vf[0]);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) mma32(vf, pf[t], o[t][d]);
+      for (int dg = 0; dg < ND / VG; ++dg) {
+        if (dg + 1 < ND / VG) vread(dg + 1, vf[(dg + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < VG; ++j)
+#pragma unroll
+          for (int t = 0; t < QT; ++t) mma32(vf[dg & 1][j], pf[t], o[t][dg * VG + j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     }
