@@ -59,12 +59,18 @@ def _vt_column(s):
 
 
 class Stages:
-    def __init__(self, seed=51):
+    def __init__(self, seed=51, key_scale=None):
         from vla_flow_matching_amd import binding
         self.w = W1.replace(name=f"pi0_bf16_b1_stages_s{seed}", seed=seed)
         # nonzero norm weights, so the (1 + w) folds are exercised
         self.blob = synth.make_weights(self.w.shape, seed=seed, dtype="bf16", norm_std=0.1)
         self.inputs = synth.make_inputs(self.w)
+        if key_scale is not None:
+            # prefix key rows scaled per position (every layer), rounded to
+            # bf16 again so that the library and the oracle see the same keys
+            kv = self.inputs["prefix_kv"]
+            L = kv.shape[3]
+            kv[:, 0] = synth.round_bf16(kv[:, 0] * key_scale(np.arange(L))[None, None, :, None, None]).reshape(kv[:, 0].shape)
         cfg = binding.make_config(self.w.shape, "bf16", max_batch=1, max_prefix_len=1024, max_steps=4)
         _say(f"create pi0 bf16 B=1 (stages) seed={seed}")
         self.ex = binding.Expert(cfg, self.blob)
@@ -192,3 +198,73 @@ def test_head_and_euler_update(st):
     h1 = h1.cpu().numpy().astype(np.float64).reshape(S, -1)
     ref = st.inputs["noise"][0].astype(np.float64) - st.orc.stage_head(h1)
     check_stage(x1.cpu().numpy()[0], ref, "final norm + action_out_proj + Euler (N=1)")
+
+
+# Key blocks whose scores grow (or shrink) from block to block by more than
+# the softmax's reference slack (2^8).  With growing scores the reference
+# maximum of a query moves 3 to 9 times after the first 64-key block (median
+# 6, counted on the host with the oracle's layer-0 queries), so the rescale
+# of the running sum and outputs runs mid-sequence; with shrinking scores it
+# moves at most twice and the later probabilities underflow.  Scores reach
+# about 180 in log2 units.
+@pytest.fixture(scope="module", params=["growing", "shrinking"])
+def st_moving(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    blocks = (np.arange(1024) // 64).astype(np.float32)
+    scale = (lambda pos: 1.0 + 4.0 * blocks[pos]) if request.param == "growing" else \
+            (lambda pos: 1.0 + 4.0 * (12.0 - np.minimum(blocks[pos], 12.0)))
+    c = Stages(seed=53, key_scale=scale)
+    c.kind = request.param
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("valid", [816, 700])
+def test_attention_reference_moves(st_moving, valid):
+    st = st_moving
+    q, k, v = st.qkv(valid, 0)
+    got = st.read(valid, "attention", 0, "attn_out").reshape(S, QD)
+    kp, vp = st.prefix(0)
+    ref = st.orc.stage_attention(q, k, v, kp, vp, valid)
+    check_stage(got, ref, f"layer 0 attention, {st.kind} key scale, valid {valid}")
+
+
+def test_attention_reference_moves_unsplit_batch32():
+    # the same growing key scale at batch 32, where 4 x 32 = 128 query
+    # blocks run the attention without key splits (the batch-64 kernel
+    # configuration), ragged valid lengths; three samples against the oracle
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from vla_flow_matching_amd import binding
+    B = 32
+    w = W1.replace(name="pi0_bf16_b32_stages", batch=B, seed=54)
+    blob = synth.make_weights(w.shape, seed=54, dtype="bf16", norm_std=0.1)
+    inputs = synth.make_inputs(w)
+    blocks = (np.arange(inputs["prefix_kv"].shape[3]) // 64).astype(np.float32)
+    kv = inputs["prefix_kv"]
+    kv[0, 0] = synth.round_bf16(kv[0, 0] * (1.0 + 4.0 * blocks)[None, :, None, None]).reshape(kv[0, 0].shape)
+    inputs["valid_len"][:] = 816 - (np.arange(B) * 23) % 300
+    cfg = binding.make_config(w.shape, "bf16", max_batch=B, max_prefix_len=816, max_steps=4)
+    _say("create pi0 bf16 B=32 (unsplit attention)")
+    ex = binding.Expert(cfg, blob)
+    try:
+        dev = binding.device_inputs(inputs, "bf16")
+        rng = np.random.default_rng(54)
+        x = torch.from_numpy(rng.standard_normal((B, w.shape.horizon, w.shape.action_dim)).astype(np.float32)).cuda()
+        t = float(np.float32(0.7))
+        args = (dev["prefix_kv"], dev["valid_len"], dev["state"], x, t)
+        _say("debug read B=32 qkv / vt / attn_out at layer 0")
+        qk = ex.debug_until(*args, "qkv", 0, "qk").float().cpu().numpy().astype(np.float64).reshape(B, S, QD + DH)
+        vt = ex.debug_until(*args, "qkv", 0, "vt").float().cpu().numpy().astype(np.float64).reshape(B, DH, -1)
+        out = ex.debug_until(*args, "attention", 0, "attn_out").float().cpu().numpy().astype(np.float64).reshape(B, S, QD)
+        orc = oracle.Oracle(w.shape, blob)
+        for b in (0, 13, 31):
+            valid = int(inputs["valid_len"][b])
+            kp = inputs["prefix_kv"][0, 0, b, :, 0, :].astype(np.float64)
+            vp = inputs["prefix_kv"][0, 1, b, :, 0, :].astype(np.float64)
+            v = vt[b][:, _vt_column(np.arange(S))].T
+            ref = orc.stage_attention(qk[b, :, :QD], qk[b, :, QD:], v, kp, vp, valid)
+            check_stage(out[b], ref, f"B=32 layer 0 attention, growing key scale, sample {b} valid {valid}")
+    finally:
+        ex.close()
