@@ -21,15 +21,17 @@
 // 16-byte accesses and shared by the waves, double-buffered so the global
 // loads of block i+1 overlap the matrix-core work on block i.  A wave computes S^T = K Q^T, so a
 // lane holds the scores of its own query (lane % 16); the online softmax runs
-// in float32 in registers and O^T = V^T P^T reuses those probabilities
+// in float32 in registers, in base 2 against a reference maximum that moves
+// only when a score passes it by 2^8, and O^T = V^T P^T reuses those
+// probabilities
 // directly as the MFMA operand.  The prefix values are transposed once per
 // call by transpose_v_kernel, the suffix values are written transposed by the
 // q/k/v projection.  Masked keys get probability exactly 0; padded prefix keys
 // are never read from the caller's cache (zeros are used instead).
 //
 // With splits > 1 (small batches) the key blocks of a sample are divided into
-// splits; each split writes its running max, sum and unnormalised output and
-// attn_combine_kernel merges them in split order.
+// splits; each split writes its reference maximum (log2 units), sum and
+// unnormalised output and attn_combine_kernel merges them in split order.
 //
 // Block order: the grid is 1-D and blocks are dealt round-robin to the 8 XCDs
 // (block L runs on XCD L % 8).  Work unit u = (b * splits + split) * tiles +
@@ -66,9 +68,9 @@ struct AttnArgs {
 
 // Per dtype: KB keys per staged block, NW waves per block, QT 16-query tiles
 // per wave (NW * QT * 16 = 128 queries per block).  Two query tiles per wave
-// (4 waves) halve the LDS fragment reads per query but need about 440
-// registers per lane at head_dim 256 and measured slower than 8 waves of one
-// tile, which is what both dtypes use.
+// (4 waves) halve the LDS fragment reads per query but need more than the 512
+// registers a lane can hold at head_dim 256 (they spill to scratch), so both
+// dtypes use 8 waves of one tile.
 template <typename T> struct AttnCfg;
 template <> struct AttnCfg<bf16> { static constexpr int KB = 64, NW = 8, QT = 1; };
 template <> struct AttnCfg<float> { static constexpr int KB = 32, NW = 8, QT = 1; };
