@@ -154,16 +154,26 @@ def run_prefill(name: str, steps: int, warmup: int, timing_calls: int = 2):
             "kernels": kern}
 
 
+def code_text(src: bytes) -> bytes:
+    """C/C++ source with comments and whitespace runs removed (the sources
+    hold no string literal with a comment marker in it)."""
+    import re
+    src = re.sub(rb"/\*.*?\*/", b" ", src, flags=re.S)
+    src = re.sub(rb"//[^\n]*", b" ", src)
+    return re.sub(rb"\s+", b" ", src).strip()
+
+
 def csrc_digest() -> str:
-    """sha256 over the HIP sources and the C header, to tell whether kernel code
-    changed since HBM byte counters were taken."""
+    """sha256 over the code (comments and layout stripped) of the HIP sources
+    and the C header, to tell whether kernel code changed since HBM byte
+    counters were taken."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vla_flow_matching_amd", "csrc")
     # the kernels' sources and the header (not the C++ driver that only calls the ABI)
     for p in sorted(f for f in os.listdir(csrc) if f != "denoise_driver.cpp") + ["../../include/pi0x.h"]:
         with open(os.path.join(csrc, p), "rb") as f:
-            h.update(p.encode() + b"\0" + f.read())
+            h.update(p.encode() + b"\0" + code_text(f.read()))
     return h.hexdigest()
 
 
