@@ -126,3 +126,28 @@ def test_full_bf16_b64_longest_prefix(gpu):
             check_close(out[b], ref[i], "bf16", f"pi0 bf16 B=64 L=1024 valid {int(inp['valid_len'][b])} sample {b}")
     finally:
         ex.close()
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_growing_key_scores_move_the_softmax_reference(gpu, dtype):
+    # prefix key rows scaled by 1, 7, 13, 19 per group of 16 keys.  In float32
+    # (32-key blocks) the second block's scores pass the first block's
+    # maximum by more than the softmax's 2^8 slack, so the reference moves
+    # mid-sequence; bf16 stages all 64 keys as one block.  End to end against
+    # the oracle at each dtype's bar (float32: 1e-4)
+    from vla_flow_matching_amd import binding
+    w = synth.Workload("tiny_moving", TINY, dtype, 2, 64, 2, seed=65)
+    ex, blob = _handle(TINY, dtype, 2, 64, seed=65)
+    try:
+        inp = synth.make_inputs(w)
+        scale = (1.0 + 6.0 * (np.arange(64) // 16)).astype(np.float32)
+        kv = inp["prefix_kv"]
+        kv[:, 0] = kv[:, 0] * scale[None, None, :, None, None]
+        if dtype == "bf16":
+            kv[:, 0] = synth.round_bf16(kv[:, 0]).reshape(kv[:, 0].shape)
+        d = binding.device_inputs(inp, dtype)
+        _say(f"denoise {dtype} growing key scale")
+        out = ex.denoise(d["prefix_kv"], d["valid_len"], d["state"], d["noise"], 2).cpu().numpy()
+        check_close(out, oracle.Oracle(TINY, blob).denoise_batch(inp, 2), dtype, f"tiny {dtype} growing key scores")
+    finally:
+        ex.close()
