@@ -722,29 +722,34 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_tile_kernel(GemmArgs g, E
     if (kt + ST - 1 < KI) issue(kt + ST - 1);
     const bf16* sa = ring + (kt % ST) * STAGE + (wm * TM * 16 + fr) * BK;
     const bf16* sb = ring + (kt % ST) * STAGE + BM * BK + (wn * TN * 16 + fr) * BK;
-    // Every fragment of the slice is read before its first MFMA: the
-    // scheduling barrier keeps the compiler from sinking the reads next to
-    // their MFMAs (which it does to save registers, exposing one LDS round
-    // trip per 32-wide K step); one round trip per slice remains.  Repeated
-    // launches on cache-resident operands ran 2-13% faster this way; inside
-    // the denoise loop and the prefix pass the difference is within noise.
+    // The fragments of the slice's first 32-wide K step are read, then the
+    // second step's reads go out while the first step's MFMAs run.  (The
+    // compiler counts the LDS DMA in flight against the LDS counter, so
+    // before the first MFMA it waits for every LDS read issued so far; the
+    // second step's reads therefore follow that wait.  With all 16 reads
+    // ahead of the MFMAs, each slice waited for all of them.)  The
+    // scheduling barriers keep this order against the compiler's habit of
+    // sinking each read next to its MFMA.
     bf16x8 af[BK / 32][TM], bfr[BK / 32][TN];
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
+    auto read_step = [&](int kk) {
       const int pos = ((kk * 4 + fq) ^ sw) * 8;
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[kk][i] = *reinterpret_cast<const bf16x8*>(sa + i * 16 * BK + pos);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[kk][j] = *reinterpret_cast<const bf16x8*>(sb + j * 16 * BK + pos);
-    }
+    };
+    read_step(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk)
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      if (kk + 1 < BK / 32) read_step(kk + 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // every wave is done reading the ring before it is reused for the epilogue
   __builtin_amdgcn_s_waitcnt(0);
