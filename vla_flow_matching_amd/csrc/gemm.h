@@ -411,6 +411,22 @@ struct EpiEuler {
 
 // inv_rms of rows m0 .. m0+n-1 into s_inv (threads < n), from the partials
 // (16-byte loads, eight in flight, when the partial count is a multiple of 4).
+__device__ __forceinline__ float row_inv_rms(const GemmArgs& g, int m0, int t) {
+  float s = 0.f;
+  if (m0 + t < g.M) {
+    const float* p = g.ssq_in + (size_t)(m0 + t) * g.ssq_np;
+    if (g.ssq_np % 4 == 0) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int i = 0; i < g.ssq_np; i += 4) acc += *reinterpret_cast<const f32x4*>(p + i);
+      s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    } else {
+      for (int i = 0; i < g.ssq_np; ++i) s += p[i];
+    }
+  }
+  return 1.0f / sqrtf(s / (float)g.norm_dim + g.norm_eps);
+}
+
 __device__ __forceinline__ void row_scale_prologue(const GemmArgs& g, int m0, int n, float* s_inv) {
   const int t = threadIdx.x;
   if (t < n) {
@@ -657,9 +673,23 @@ constexpr int tile_waves_per_simd() {
   return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
 
+// A ring of exactly 80 KiB (the 64x256 tiles of two stages) lets two blocks
+// share a CU only with no static LDS beside it: such a kernel keeps each
+// row's inverse RMS in a register through the main loop and stages it in the
+// last bytes of the ring for the epilogue.
+template <int BM, int BN, int BK, int ST, int NWM, int NWN>
+constexpr bool tile_ring_staged() {
+  return tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>() == 80 * 1024;
+}
+template <int BM, int BN, int BK, int ST, int NWM, int NWN>
+constexpr int tile_waves_per_simd_hint() {
+  if constexpr (tile_ring_staged<BM, BN, BK, ST, NWM, NWN>()) return 2 * NWM * NWN / 4;
+  else return tile_waves_per_simd<BM, BN, BK, ST, NWM, NWN>();
+}
+
 template <int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(NWM * NWN * 64) __attribute__((amdgpu_waves_per_eu(
-    tile_waves_per_simd<BM, BN, BK, ST, NWM, NWN>(), tile_waves_per_simd<BM, BN, BK, ST, NWM, NWN>()))) void
+    tile_waves_per_simd_hint<BM, BN, BK, ST, NWM, NWN>(), tile_waves_per_simd_hint<BM, BN, BK, ST, NWM, NWN>()))) void
 gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n, int group_m) {
   constexpr int NT = NWM * NWN * 64;
   constexpr int TM = BM / NWM / 16, TN = BN / NWN / 16;  // 16x16 MFMA tiles per wave
@@ -673,7 +703,17 @@ gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n, int group_m) {
   static_assert((size_t)(NT / 64) * 32 * ELD * 4 <= tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>(), "epilogue staging must fit");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* ring = reinterpret_cast<bf16*>(smem_raw);
-  __shared__ float s_inv[BM];
+  constexpr bool STAGED = tile_ring_staged<BM, BN, BK, ST, NWM, NWN>();
+  static_assert(!STAGED || (size_t)(NT / 64) * 32 * ELD * 4 + BM * 4 <= tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>(),
+                "staged inverse RMS must clear the epilogue strips");
+  float* s_inv;
+  if constexpr (STAGED) {
+    s_inv = reinterpret_cast<float*>(smem_raw + tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>() - BM * 4);
+  } else {
+    __shared__ float s_inv_static[BM];
+    s_inv = s_inv_static;
+  }
+  float inv_reg = 0.f;  // STAGED: this thread's row (tid < BM) until the epilogue
 
   // tile (and K range) of this block
   const int S = g.splits;
@@ -720,7 +760,13 @@ gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p)
     if (p < KI) issue(p);
-  if constexpr (Epi::kRowScale) row_scale_prologue(g, m0, BM, s_inv);
+  if constexpr (Epi::kRowScale) {
+    if constexpr (STAGED) {
+      if (tid < BM) inv_reg = row_inv_rms(g, m0, tid);
+    } else {
+      row_scale_prologue(g, m0, BM, s_inv);
+    }
+  }
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -768,6 +814,10 @@ gemm_tile_kernel(GemmArgs g, Epi epi, int tiles_m, int tiles_n, int group_m) {
   // every wave is done reading the ring before it is reused for the epilogue
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (STAGED && Epi::kRowScale) {
+    if (tid < BM) s_inv[tid] = inv_reg;
+    __syncthreads();
+  }
 
   // Epilogue through LDS, one 32-row strip (two 16-row MFMA tiles) of the wave
   // tile at a time: the strip is written in the MFMA layout (element e of tile

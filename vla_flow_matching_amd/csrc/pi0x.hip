@@ -326,19 +326,26 @@ pi0x_status launch_gemm_cfg(pi0x_expert* h, hipStream_t s, GemmArgs g, const Epi
 template <int BN>
 constexpr int kGroupM = BN == 128 ? 8 : 2;
 
-template <int BN, int ST, class Epi>
-pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi) {
-  constexpr int BM = 128, BK = 64;
+template <int BN, int ST, class Epi, int BM = 128, int NWM = 2, int NWN = 2>
+pi0x_status launch_gemm_tile_cfg(hipStream_t s, GemmArgs g, const Epi& epi, int group_m = kGroupM<BN>) {
+  constexpr int BK = 64;
   const int tm = (g.M + BM - 1) / BM, tn = g.N / BN;
   const int blocks = 8 * ((tm * tn * g.splits + 7) / 8);
-  constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST>();
-  gemm_tile_kernel<BM, BN, BK, ST, 2, 2, Epi><<<dim3(blocks), dim3(256), smem, s>>>(g, epi, tm, tn, kGroupM<BN>);
+  constexpr size_t smem = tile_smem_bytes<BM, BN, BK, ST, NWM, NWN>();
+  gemm_tile_kernel<BM, BN, BK, ST, NWM, NWN, Epi><<<dim3(blocks), dim3(256), smem, s>>>(g, epi, tm, tn, group_m);
   PI0X_HIP(hipGetLastError());
   return PI0X_OK;
 }
 
 template <class Epi>
 pi0x_status launch_gemm_tile(hipStream_t s, GemmArgs g, const Epi& epi) {
+  if constexpr (std::is_same_v<Epi, EpiQkvRope<bf16>>) {
+    // 64x256 tiles (4 waves of 64x64, two blocks per CU) when they make one
+    // nearly full round of the chip's 512 resident blocks: batch 64's 3264
+    // rows are 51 x 10 = 510 tiles, where 128x64 tiles make 1.35 rounds
+    const int t64 = ((g.M + 63) / 64) * (g.N / 256);
+    if (g.N % 256 == 0 && t64 > 448 && t64 <= 512) return launch_gemm_tile_cfg<256, 2, Epi, 64, 1, 4>(s, g, epi, 8);
+  }
   if (g.N > 4096 && g.N % 128 == 0 && !Epi::kSsq) return launch_gemm_tile_cfg<128, 2>(s, g, epi);
   if (g.K >= 2048) return launch_gemm_tile_cfg<64, 3>(s, g, epi);
   return launch_gemm_tile_cfg<64, 2>(s, g, epi);
@@ -440,6 +447,8 @@ pi0x_status allow_tile_smem() {
 }
 
 pi0x_status allow_tile_smem_all() {
+  PI0X_HIP(hipFuncSetAttribute((const void*)gemm_tile_kernel<64, 256, 64, 2, 1, 4, EpiQkvRope<bf16>>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)tile_smem_bytes<64, 256, 64, 2, 1, 4>()));
   PI0X_TRY(allow_tile_smem<EpiStore<float>>());
   PI0X_TRY(allow_tile_smem<EpiStore<bf16>>());
   PI0X_TRY(allow_tile_smem<EpiSuffixRows<bf16>>());
