@@ -409,8 +409,8 @@ struct EpiEuler {
   __device__ __forceinline__ void ssq(int, int, float) const {}
 };
 
-// inv_rms of rows m0 .. m0+n-1 into s_inv (threads < n), from the partials
-// (16-byte loads, eight in flight, when the partial count is a multiple of 4).
+// inv_rms of row m0 + t from its partial sums of squares (16-byte loads,
+// eight in flight, when the partial count is a multiple of 4).
 __device__ __forceinline__ float row_inv_rms(const GemmArgs& g, int m0, int t) {
   float s = 0.f;
   if (m0 + t < g.M) {
@@ -427,6 +427,8 @@ __device__ __forceinline__ float row_inv_rms(const GemmArgs& g, int m0, int t) {
   return 1.0f / sqrtf(s / (float)g.norm_dim + g.norm_eps);
 }
 
+// inv_rms of rows m0 .. m0+n-1 into s_inv (threads < n): the same arithmetic
+// as row_inv_rms, written to LDS.
 __device__ __forceinline__ void row_scale_prologue(const GemmArgs& g, int m0, int n, float* s_inv) {
   const int t = threadIdx.x;
   if (t < n) {
